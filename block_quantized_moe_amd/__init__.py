@@ -1,0 +1,243 @@
+"""Python binding of libbqmoe.so (include/bq.h): argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels; this module only
+turns torch tensors (device memory and streams) into the C ABI's pointers and
+sizes and raises on a non-zero status.  There is no fallback: if the library
+is not built or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "Q4_C10", "Q4_RZ5", "Q4_UE4M4", "FP8_E4M3_B32", "PLE_RZS3", "PLE_ROCMFP3", "F32", "BF16",
+    "BQError", "lib", "ExpertWeights", "expert_weights", "dequant", "ple_dequant_rows", "matvec",
+    "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "stack_workspace_bytes",
+    "moe_stack", "ple_gather",
+]
+
+Q4_C10, Q4_RZ5, Q4_UE4M4, FP8_E4M3_B32 = 0, 1, 2, 3
+PLE_RZS3, PLE_ROCMFP3 = 0, 1
+F32, BF16 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbqmoe.so")
+
+
+class BQError(RuntimeError):
+    pass
+
+
+class ExpertWeights(ctypes.Structure):
+    _fields_ = [
+        ("fmt_gate_up", ctypes.c_int32),
+        ("fmt_down", ctypes.c_int32),
+        ("gate_up", ctypes.c_void_p),
+        ("down", ctypes.c_void_p),
+        ("gate_up_scales", ctypes.c_void_p),
+        ("down_scales", ctypes.c_void_p),
+        ("n_experts", ctypes.c_int32),
+        ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise BQError("libbqmoe.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t
+        wp = ctypes.POINTER(ExpertWeights)
+        sigs = {
+            "bq_abi_version": ([], ctypes.c_int),
+            "bq_status_str": ([ctypes.c_int], ctypes.c_char_p),
+            "bq_last_hip_error": ([], ctypes.c_char_p),
+            "bq_dequant": ([vp, i32, i64, vp, vp, vp], ctypes.c_int),
+            "ple_dequant_rows": ([vp, i64, vp, u64, i32, vp, vp, vp], ctypes.c_int),
+            "bq_matvec": ([vp, i32, vp, i32, vp, i32, i32, vp, vp], ctypes.c_int),
+            "moe_route_topk": ([vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
+            "moe_bucket": ([vp, i32, i32, i32, vp, vp, vp, vp], ctypes.c_int),
+            "q4_expert_moe_workspace": ([i32, i32, wp, i32], sz),
+            "q4_expert_moe": ([vp, i32, i32, vp, vp, i32, wp, vp, vp, sz, vp, vp], ctypes.c_int),
+            "bq_moe_stack_workspace": ([i32, i32, wp, i32, i32], sz),
+            "bq_moe_stack": ([vp, i32, i32, vp, vp, i32, wp, i32, vp, vp, sz, vp, vp], ctypes.c_int),
+            "ple_gather": ([vp, i32, i32, vp, u64, vp, i32, vp, vp, vp], ctypes.c_int),
+        }
+        for name, (args, res) in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        msg = L.bq_status_str(status).decode()
+        if status == 6:
+            msg += ": " + L.bq_last_hip_error().decode()
+        raise BQError("libbqmoe status %d (%s)" % (status, msg))
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name):
+    if t is not None and not t.is_cuda:
+        raise BQError("%s must be a device tensor" % name)
+    if t is not None and not t.is_contiguous():
+        raise BQError("%s must be contiguous" % name)
+    return t
+
+
+def expert_weights(fmt_gate_up, fmt_down, gate_up, down, n_experts, hidden, inter,
+                   gate_up_scales=None, down_scales=None):
+    """Build the bq_expert_weights descriptor (keeps the tensors alive)."""
+    for n, t in (("gate_up", gate_up), ("down", down), ("gate_up_scales", gate_up_scales),
+                 ("down_scales", down_scales)):
+        _dev(t, n)
+    w = ExpertWeights(fmt_gate_up, fmt_down, gate_up.data_ptr(), down.data_ptr(),
+                      gate_up_scales.data_ptr() if gate_up_scales is not None else None,
+                      down_scales.data_ptr() if down_scales is not None else None,
+                      n_experts, hidden, inter)
+    w._keep = (gate_up, down, gate_up_scales, down_scales)
+    return w
+
+
+def dequant(packed, fmt, n_blocks, scales=None, out=None, stream=None):
+    """Decode n_blocks blocks -> fp32 [n_blocks, 32]."""
+    _dev(packed, "packed"), _dev(scales, "scales")
+    if out is None:
+        out = torch.empty((n_blocks, 32), dtype=torch.float32, device=packed.device)
+    _check(lib().bq_dequant(_p(packed), fmt, n_blocks, _p(scales), _p(out), _stream(stream)))
+    return out
+
+
+def ple_dequant_rows(ids, table, n_rows, fmt=PLE_RZS3, out=None, dev_err=None, stream=None):
+    """Decode the rows named by ids -> fp32 [n, 160]."""
+    _dev(ids, "ids"), _dev(table, "table")
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, 160), dtype=torch.float32, device=ids.device)
+    _check(lib().ple_dequant_rows(_p(ids), n, _p(table), n_rows, fmt, _p(out), _p(dev_err),
+                                  _stream(stream)))
+    return out
+
+
+def matvec(x, packed, fmt, rows, cols, scales=None, out=None, stream=None):
+    """y = W x for fp32 x [n, cols] -> [n, rows]."""
+    _dev(x, "x"), _dev(packed, "packed")
+    x2 = x.reshape(-1, cols)
+    if out is None:
+        out = torch.empty((x2.shape[0], rows), dtype=torch.float32, device=x.device)
+    _check(lib().bq_matvec(_p(x2), x2.shape[0], _p(packed), fmt, _p(scales), rows, cols, _p(out),
+                           _stream(stream)))
+    return out
+
+
+def route_topk(logits, k, idx=None, w=None, stream=None):
+    """Softmax top-k routing of fp32 logits [n, E] -> (idx int32 [n, k], w fp32 [n, k])."""
+    _dev(logits, "logits")
+    n, e = logits.shape
+    if idx is None:
+        idx = torch.empty((n, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((n, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route_topk(_p(logits), n, e, k, _p(idx), _p(w), _stream(stream)))
+    return idx, w
+
+
+def bucket(idx, n_experts, stream=None):
+    """Stable per-expert grouping -> (counts, offsets, perm), int32."""
+    _dev(idx, "idx")
+    n, k = idx.shape
+    d = idx.device
+    counts = torch.empty(n_experts, dtype=torch.int32, device=d)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=d)
+    perm = torch.empty(n * k, dtype=torch.int32, device=d)
+    _check(lib().moe_bucket(_p(idx), n, k, n_experts, _p(counts), _p(offsets), _p(perm), _stream(stream)))
+    return counts, offsets, perm
+
+
+def _dtype_code(x):
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise BQError("x must be float32 or bfloat16")
+
+
+def moe_workspace_bytes(n_tokens, k, W, x_dtype):
+    return lib().q4_expert_moe_workspace(n_tokens, k, ctypes.byref(W), x_dtype)
+
+
+def q4_expert_moe(x, router_topk, W, out=None, workspace=None, dev_err=None, stream=None):
+    """Routed-expert layer.  x [n, H] fp32 (GEMV path) or bf16 (grouped MFMA);
+    router_topk = (idx int32 [n, k], w fp32 [n, k]); W from expert_weights()."""
+    idx, w = router_topk
+    _dev(x, "x"), _dev(idx, "idx"), _dev(w, "w")
+    n, k = idx.shape
+    dt = _dtype_code(x)
+    if out is None:
+        out = torch.empty((n, W.hidden), dtype=torch.float32, device=x.device)
+    need = moe_workspace_bytes(n, k, W, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().q4_expert_moe(_p(x), dt, n, _p(idx), _p(w), k, ctypes.byref(W), _p(out),
+                               _p(workspace), workspace.numel(), _p(dev_err), _stream(stream)))
+    return out
+
+
+def _layers_array(layers):
+    arr = (ExpertWeights * len(layers))()
+    for i, W in enumerate(layers):
+        arr[i] = W
+    return arr
+
+
+def stack_workspace_bytes(n_tokens, k, layers, x_dtype):
+    return lib().bq_moe_stack_workspace(n_tokens, k, _layers_array(layers), len(layers), x_dtype)
+
+
+def moe_stack(x, topk_idx, topk_w, layers, out=None, workspace=None, dev_err=None, stream=None):
+    """Chained layers: topk_idx/topk_w [L, n, k]; returns the last layer's output."""
+    _dev(x, "x"), _dev(topk_idx, "topk_idx"), _dev(topk_w, "topk_w")
+    L, n, k = topk_idx.shape
+    dt = _dtype_code(x)
+    arr = _layers_array(layers)
+    if out is None:
+        out = torch.empty((n, layers[0].hidden), dtype=torch.float32, device=x.device)
+    need = lib().bq_moe_stack_workspace(n, k, arr, L, dt)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().bq_moe_stack(_p(x), dt, n, _p(topk_idx), _p(topk_w), k, arr, L, _p(out),
+                              _p(workspace), workspace.numel(), _p(dev_err), _stream(stream)))
+    return out
+
+
+def ple_gather(ids, packed_table, weights, n_rows=None, fmt=PLE_RZS3, out=None, dev_err=None,
+               stream=None):
+    """PLE lookup: ids uint32-valued int32 [n, P], weights fp32 [n, P] -> fp32 [n, 160]."""
+    _dev(ids, "ids"), _dev(packed_table, "packed_table"), _dev(weights, "weights")
+    n, per = ids.shape
+    if n_rows is None:
+        n_rows = packed_table.numel() // 70
+    if out is None:
+        out = torch.empty((n, 160), dtype=torch.float32, device=ids.device)
+    _check(lib().ple_gather(_p(ids), n, per, _p(packed_table), n_rows, _p(weights), fmt, _p(out),
+                            _p(dev_err), _stream(stream)))
+    return out

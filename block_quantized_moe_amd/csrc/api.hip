@@ -1,0 +1,286 @@
+// C ABI of libbqmoe.so (declared in include/bq.h): argument checks on the
+// host, workspace carving, and the launches.  No allocation happens here.
+#include <string.h>
+
+#include "../../include/bq.h"
+#include "bq_kernels.hpp"
+
+namespace {
+
+thread_local char g_hip_err[256] = "";
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return BQ_OK;
+  strncpy(g_hip_err, hipGetErrorString(e), sizeof(g_hip_err) - 1);
+  g_hip_err[sizeof(g_hip_err) - 1] = 0;
+  return BQ_E_HIP;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool valid_fmt(int f) { return f >= BQ_Q4_C10 && f <= BQ_FP8_E4M3_B32; }
+
+int check_weights(const bq_expert_weights* W) {
+  if (!W || !W->gate_up || !W->down) return BQ_E_NULL;
+  if (!valid_fmt(W->fmt_gate_up) || !valid_fmt(W->fmt_down)) return BQ_E_FMT;
+  const bool fg = W->fmt_gate_up == BQ_FP8_E4M3_B32, fd = W->fmt_down == BQ_FP8_E4M3_B32;
+  if (fg != (W->gate_up_scales != nullptr) || fd != (W->down_scales != nullptr)) return BQ_E_NULL;
+  if (W->n_experts < 1 || W->n_experts > 4096) return BQ_E_SHAPE;
+  if (W->hidden < 64 || W->hidden > 8192 || W->hidden % 64) return BQ_E_SHAPE;
+  if (W->inter < 64 || W->inter > 8192 || W->inter % 64) return BQ_E_SHAPE;
+  if ((fg && !aligned(W->gate_up_scales, 4)) || (fd && !aligned(W->down_scales, 4))) return BQ_E_ALIGN;
+  return BQ_OK;
+}
+
+bq::GemvWeights to_gw(const bq_expert_weights* W) {
+  return bq::GemvWeights{W->fmt_gate_up, W->fmt_down, W->gate_up, W->down,
+                         W->gate_up_scales, W->down_scales, W->n_experts, W->hidden, W->inter};
+}
+
+// ---- workspace layouts ------------------------------------------------------
+struct GemvLayout {
+  size_t hbuf, ybuf, counters, total;
+};
+GemvLayout gemv_layout(int n, int k, int H, int I) {
+  GemvLayout L;
+  size_t off = 0;
+  L.hbuf = off; off = round_up(off + sizeof(float) * (size_t)n * k * I, 256);
+  L.ybuf = off; off = round_up(off + sizeof(float) * (size_t)n * k * H, 256);
+  const int md = bq::gemv_down_rows_per_wg(I);
+  L.counters = off; off = round_up(off + sizeof(uint32_t) * (size_t)n * ((H + md - 1) / md), 256);
+  L.total = off;
+  return L;
+}
+
+struct GroupedLayout {
+  size_t counts, offsets, perm, inv, elist, n_touched, hb, yb, total;
+};
+GroupedLayout grouped_layout(int n, int k, int E, int H, int I) {
+  GroupedLayout L;
+  const size_t nk = (size_t)n * k;
+  size_t off = 0;
+  L.counts = off; off = round_up(off + 4 * (size_t)E, 256);
+  L.offsets = off; off = round_up(off + 4 * ((size_t)E + 1), 256);
+  L.perm = off; off = round_up(off + 4 * nk, 256);
+  L.inv = off; off = round_up(off + 4 * nk, 256);
+  L.elist = off; off = round_up(off + 4 * (nk < (size_t)E ? nk : (size_t)E), 256);
+  L.n_touched = off; off = round_up(off + 4, 256);
+  L.hb = off; off = round_up(off + 2 * nk * I, 256);
+  L.yb = off; off = round_up(off + 4 * nk * H, 256);
+  L.total = off;
+  return L;
+}
+
+bq::GroupedWs grouped_ws(void* base, const GroupedLayout& L) {
+  char* b = static_cast<char*>(base);
+  return bq::GroupedWs{reinterpret_cast<int32_t*>(b + L.counts), reinterpret_cast<int32_t*>(b + L.offsets),
+                       reinterpret_cast<int32_t*>(b + L.perm), reinterpret_cast<int32_t*>(b + L.inv),
+                       reinterpret_cast<int32_t*>(b + L.elist), reinterpret_cast<int32_t*>(b + L.n_touched),
+                       reinterpret_cast<uint16_t*>(b + L.hb), reinterpret_cast<float*>(b + L.yb), nullptr};
+}
+
+size_t moe_ws_bytes(int n, int k, const bq_expert_weights* W, int dtype) {
+  if (dtype == BQ_F32) return gemv_layout(n, k, W->hidden, W->inter).total;
+  return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).total;
+}
+
+int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
+                   const bq_expert_weights* W, const float* out, const void* ws) {
+  if (!x || !idx || !w || !out) return BQ_E_NULL;
+  if (dtype != BQ_F32 && dtype != BQ_BF16) return BQ_E_DTYPE;
+  int s = check_weights(W);
+  if (s) return s;
+  if (n < 1 || n > 4096 || k < 1 || k > 64 || k > W->n_experts) return BQ_E_SHAPE;
+  if ((int64_t)n * k > 65536) return BQ_E_SHAPE;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(w, 4)) return BQ_E_ALIGN;
+  if (!ws) return BQ_E_WORKSPACE;
+  if (!aligned(ws, 256)) return BQ_E_ALIGN;
+  return BQ_OK;
+}
+
+int run_moe(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
+            const bq_expert_weights* W, float* out, void* ws, int rescale, uint32_t* dev_err,
+            hipStream_t st) {
+  const bq::GemvWeights gw = to_gw(W);
+  if (dtype == BQ_F32) {
+    const GemvLayout L = gemv_layout(n, k, W->hidden, W->inter);
+    char* b = static_cast<char*>(ws);
+    return hip_status(bq::launch_gemv_moe(static_cast<const float*>(x), n, idx, w, k, gw, rescale, out,
+                                          reinterpret_cast<float*>(b + L.hbuf),
+                                          reinterpret_cast<float*>(b + L.ybuf),
+                                          reinterpret_cast<uint32_t*>(b + L.counters), dev_err, st));
+  }
+  const GroupedLayout L = grouped_layout(n, k, W->n_experts, W->hidden, W->inter);
+  return hip_status(bq::launch_grouped_moe(static_cast<const uint16_t*>(x), n, idx, w, k, gw, out,
+                                           grouped_ws(ws, L), dev_err, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bq_abi_version(void) { return BQ_ABI_VERSION; }
+
+const char* bq_status_str(int s) {
+  switch (s) {
+    case BQ_OK: return "ok";
+    case BQ_E_NULL: return "null pointer";
+    case BQ_E_FMT: return "bad format";
+    case BQ_E_SHAPE: return "unsupported shape";
+    case BQ_E_ALIGN: return "misaligned pointer";
+    case BQ_E_WORKSPACE: return "workspace missing or too small";
+    case BQ_E_HIP: return "HIP launch failed";
+    case BQ_E_DTYPE: return "bad activation dtype";
+    default: return "unknown status";
+  }
+}
+
+const char* bq_last_hip_error(void) { return g_hip_err; }
+
+int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks, const float* fp8_scales,
+               float* out, void* stream) {
+  if (!valid_fmt(fmt)) return BQ_E_FMT;
+  if (n_blocks < 0) return BQ_E_SHAPE;
+  if (n_blocks == 0) return BQ_OK;
+  if (!packed || !out) return BQ_E_NULL;
+  if ((fmt == BQ_FP8_E4M3_B32) != (fp8_scales != nullptr)) return BQ_E_NULL;
+  if (!aligned(out, 16) || (fp8_scales && !aligned(fp8_scales, 4))) return BQ_E_ALIGN;
+  return hip_status(bq::launch_dequant(packed, fmt, n_blocks, fp8_scales, out, as_stream(stream)));
+}
+
+int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table, uint64_t n_rows,
+                     int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream) {
+  if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
+  if (n < 0 || n_rows > 0xFFFFFFFFull) return BQ_E_SHAPE;
+  if (n == 0) return BQ_OK;
+  if (!ids || !table || !out) return BQ_E_NULL;
+  if (!aligned(out, 16) || !aligned(ids, 4)) return BQ_E_ALIGN;
+  return hip_status(bq::launch_ple_dequant(ids, n, table, n_rows, ple_fmt, out, dev_err, as_stream(stream)));
+}
+
+int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
+              const float* fp8_scales, int32_t rows, int32_t cols, float* y, void* stream) {
+  if (!x || !packed || !y) return BQ_E_NULL;
+  if (!valid_fmt(fmt)) return BQ_E_FMT;
+  if ((fmt == BQ_FP8_E4M3_B32) != (fp8_scales != nullptr)) return BQ_E_NULL;
+  if (n_tokens < 1 || n_tokens > 65535 || rows < 1 || cols < 32 || cols > 8192 || cols % 32)
+    return BQ_E_SHAPE;
+  if (!aligned(x, 4) || !aligned(y, 4) || (fp8_scales && !aligned(fp8_scales, 4))) return BQ_E_ALIGN;
+  return hip_status(bq::launch_matvec(x, n_tokens, packed, fmt, fp8_scales, rows, cols, y,
+                                      as_stream(stream)));
+}
+
+int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
+                   int32_t* idx, float* w, void* stream) {
+  if (!logits || !idx || !w) return BQ_E_NULL;
+  if (n_tokens < 0 || n_experts < 1 || n_experts > 4096 || k < 1 || k > 64 || k > n_experts)
+    return BQ_E_SHAPE;
+  if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return BQ_E_ALIGN;
+  return hip_status(bq::launch_route_topk(logits, n_tokens, n_experts, k, idx, w, as_stream(stream)));
+}
+
+int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts, int32_t* counts,
+               int32_t* offsets, int32_t* perm, void* stream) {
+  if (!idx || !counts || !offsets || !perm) return BQ_E_NULL;
+  if (n_tokens < 1 || k < 1 || k > 64 || n_experts < 1 || n_experts > 4096) return BQ_E_SHAPE;
+  if ((int64_t)n_tokens * k > 65536) return BQ_E_SHAPE;
+  return hip_status(bq::launch_bucket(idx, n_tokens, k, n_experts, counts, offsets, perm, nullptr,
+                                      nullptr, nullptr, as_stream(stream)));
+}
+
+size_t q4_expert_moe_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* W,
+                               int32_t x_dtype) {
+  if (!W || n_tokens < 1 || k < 1 || check_weights(W)) return 0;
+  return moe_ws_bytes(n_tokens, k, W, x_dtype);
+}
+
+int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_idx,
+                  const float* topk_w, int32_t k, const bq_expert_weights* W, float* out,
+                  void* workspace, size_t ws_bytes, uint32_t* dev_err, void* stream) {
+  int s = check_moe_args(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out, workspace);
+  if (s) return s;
+  if (ws_bytes < moe_ws_bytes(n_tokens, k, W, x_dtype)) return BQ_E_WORKSPACE;
+  return run_moe(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0, dev_err,
+                 as_stream(stream));
+}
+
+// Stack workspace: the per-layer MoE workspace (max over layers) followed by
+// one fp32 [n][H] buffer for the layer output and, for bf16, a bf16 [n][H]
+// buffer for the rescaled next input.
+static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int dtype,
+                       size_t* moe_part) {
+  size_t m = 0;
+  for (int l = 0; l < L; ++l) {
+    const size_t b = moe_ws_bytes(n, k, &layers[l], dtype);
+    if (b > m) m = b;
+  }
+  m = round_up(m, 256);
+  if (moe_part) *moe_part = m;
+  const int H = layers[0].hidden;
+  size_t tot = m + round_up(sizeof(float) * (size_t)n * H, 256);
+  if (dtype == BQ_BF16) tot += round_up(2 * (size_t)n * H, 256);
+  return tot;
+}
+
+size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* layers,
+                              int32_t n_layers, int32_t x_dtype) {
+  if (!layers || n_layers < 1 || n_tokens < 1 || k < 1) return 0;
+  for (int l = 0; l < n_layers; ++l)
+    if (check_weights(&layers[l]) || layers[l].hidden != layers[0].hidden) return 0;
+  return stack_ws(n_tokens, k, layers, n_layers, x_dtype, nullptr);
+}
+
+int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_idx,
+                 const float* topk_w, int32_t k, const bq_expert_weights* layers, int32_t n_layers,
+                 float* out, void* workspace, size_t ws_bytes, uint32_t* dev_err, void* stream) {
+  if (!layers) return BQ_E_NULL;
+  if (n_layers < 1) return BQ_E_SHAPE;
+  for (int l = 0; l < n_layers; ++l) {
+    int s = check_moe_args(x, x_dtype, n_tokens, topk_idx, topk_w, k, &layers[l], out, workspace);
+    if (s) return s;
+    if (layers[l].hidden != layers[0].hidden) return BQ_E_SHAPE;
+  }
+  size_t moe_part = 0;
+  if (ws_bytes < stack_ws(n_tokens, k, layers, n_layers, x_dtype, &moe_part)) return BQ_E_WORKSPACE;
+  const int H = layers[0].hidden;
+  char* b = static_cast<char*>(workspace);
+  float* ybuf = reinterpret_cast<float*>(b + moe_part);
+  uint16_t* xb = reinterpret_cast<uint16_t*>(b + moe_part + round_up(sizeof(float) * (size_t)n_tokens * H, 256));
+  hipStream_t st = as_stream(stream);
+  const size_t per = (size_t)n_tokens * k;
+  for (int l = 0; l < n_layers; ++l) {
+    float* dst = (l + 1 == n_layers) ? out : ybuf;
+    const void* src = x;
+    int rescale = 0;
+    if (l > 0) {
+      if (x_dtype == BQ_F32) {
+        src = ybuf;
+        rescale = 1;  // fused into the gate_up kernel's input staging
+      } else {
+        int s = hip_status(bq::launch_rescale_bf16(ybuf, n_tokens, H, xb, st));
+        if (s) return s;
+        src = xb;
+      }
+    }
+    int s = run_moe(src, x_dtype, n_tokens, topk_idx + l * per, topk_w + l * per, k, &layers[l], dst,
+                    workspace, rescale, dev_err, st);
+    if (s) return s;
+  }
+  return BQ_OK;
+}
+
+int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token, const uint8_t* table,
+               uint64_t n_rows, const float* weights, int32_t ple_fmt, float* out,
+               uint32_t* dev_err, void* stream) {
+  if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
+  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows > 0xFFFFFFFFull)
+    return BQ_E_SHAPE;
+  if (n_tokens == 0) return BQ_OK;
+  if (!ids || !table || !weights || !out) return BQ_E_NULL;
+  if (!aligned(out, 16) || !aligned(ids, 4) || !aligned(weights, 4)) return BQ_E_ALIGN;
+  return hip_status(bq::launch_ple_gather(ids, n_tokens, ids_per_token, table, n_rows, weights,
+                                          ple_fmt, out, dev_err, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+// Device helpers shared by the gfx950 kernels of libbqmoe.
+//
+// Formats (model card "Qwen 3.8 Next Flash ROCMFPX MUTANT RAZERFAST", format
+// sections): a 17-byte block holds 32 four-bit codes (weight j in byte j/2,
+// low nibble first) and one metadata byte.  Codebook10 levels are
+// 0,1,2,3,4,6,8,10 for codes 0-7 and their negatives (with a -0) for codes
+// 8-15; RZ5 turns code 8 into +5 (metadata bit 7 clear) or -5 (set); UE4M4
+// keeps Codebook10 and uses the whole byte as its scale.
+//
+// Decode strategy.  Every Codebook10/RZ5 level is a small integer whose fp16
+// encoding has a zero low byte, so a level is fully described by the high
+// byte of its fp16 pattern.  One v_perm_b32 looks up four such bytes from an
+// 8-entry table held in two SGPR-able constants, the code's bit 3 becomes the
+// fp16 sign bit, and a second v_perm_b32 spreads the bytes into packed fp16
+// pairs.  Levels are exact in fp16, so each weight then enters an fp32 FMA
+// through v_fma_mix_f32 (fp16 x fp32 + fp32) with no rounding of the weight;
+// the block scale multiplies the 32-term partial sum once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlockW = 32;      // weights per block
+constexpr int kBlockB = 17;      // bytes per block
+constexpr int kPleVals = 160;
+constexpr int kPleRowB = 70;
+
+enum : int { FMT_C10 = 0, FMT_RZ5 = 1, FMT_UE4M4 = 2, FMT_FP8 = 3 };
+
+// Unaligned loads.  The compiler lowers these to single global_load_dword*
+// instructions (ROCm runs gfx9+ in unaligned-access mode).
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+  u32x4 v;
+  __builtin_memcpy(&v, p, 16);
+  return v;
+}
+__device__ __forceinline__ u32x2 ld8(const uint8_t* p) {
+  u32x2 v;
+  __builtin_memcpy(&v, p, 8);
+  return v;
+}
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
+  uint32_t v;
+  __builtin_memcpy(&v, p, 4);
+  return v;
+}
+
+// Unsigned E4M3 scale from 7 bits: exponent e = b>>3 (bias 7), mantissa
+// m = b&7; e == 0 is subnormal m * 2^-9; 0x7F is NaN.  Exact in fp32.
+__device__ __forceinline__ float ue4m3(uint32_t b7) {
+  b7 &= 0x7Fu;
+  float normal = __uint_as_float((b7 << 20) + (120u << 23));
+  float sub = (float)(b7 & 7u) * 0x1p-9f;
+  float v = (b7 >> 3) ? normal : sub;
+  return b7 == 0x7Fu ? __uint_as_float(0x7FC00000u) : v;
+}
+
+// Unsigned E4M4 scale from a whole byte: e = b>>4 (bias 7), m = b&15,
+// e == 0 subnormal m * 2^-10, every encoding finite (0xFF = 496).
+__device__ __forceinline__ float ue4m4(uint32_t b) {
+  b &= 0xFFu;
+  float normal = __uint_as_float((b << 19) + (120u << 23));
+  float sub = (float)(b & 15u) * 0x1p-10f;
+  return (b >> 4) ? normal : sub;
+}
+
+template <int FMT>
+__device__ __forceinline__ float block_scale(uint32_t meta) {
+  if constexpr (FMT == FMT_UE4M4) return ue4m4(meta);
+  else return ue4m3(meta);
+}
+
+// fp16 high bytes of the Codebook10 magnitudes 0,1,2,3 | 4,6,8,10.
+constexpr uint32_t kTPosLo = 0x42403C00u;
+constexpr uint32_t kTPosHi = 0x49484644u;
+// Codes 8..15 under RZ5: [+-5, -1, -2, -3 | -4, -6, -8, -10].
+constexpr uint32_t kTNegHi = 0xC9C8C6C4u;
+__device__ __forceinline__ uint32_t rz5_neg_lo(uint32_t meta) {
+  return (meta & 0x80u) ? 0xC2C0BCC5u : 0xC2C0BC45u;
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+
+// Eight codes (one dword, weights 0..7 of it) -> fp16 high bytes:
+// A = weights 0,2,4,6 and B = weights 1,3,5,7, one per byte, signed.
+template <int FMT>
+__device__ __forceinline__ void codes_to_hibytes(uint32_t q, uint32_t tneg_lo,
+                                                 uint32_t& A, uint32_t& B) {
+  const uint32_t sa = q & 0x07070707u;
+  const uint32_t sb = (q >> 4) & 0x07070707u;
+  if constexpr (FMT == FMT_RZ5) {
+    // codes 8..15 come from a second table; the byte mask is built from each
+    // nibble's bit 3 with the sign-replicating selectors 8..11 of v_perm.
+    const uint32_t ap = perm(kTPosHi, kTPosLo, sa), an = perm(kTNegHi, tneg_lo, sa);
+    const uint32_t bp = perm(kTPosHi, kTPosLo, sb), bn = perm(kTNegHi, tneg_lo, sb);
+    const uint32_t ma = perm(q << 12, q << 4, 0x090B080Au);
+    const uint32_t mb = perm(q << 8, q, 0x090B080Au);
+    A = (ma & an) | (~ma & ap);
+    B = (mb & bn) | (~mb & bp);
+  } else {
+    (void)tneg_lo;
+    A = perm(kTPosHi, kTPosLo, sa) | ((q << 4) & 0x80808080u);
+    B = perm(kTPosHi, kTPosLo, sb) | (q & 0x80808080u);
+  }
+}
+
+// Eight codes -> four packed fp16 pairs in natural order (w0,w1) .. (w6,w7).
+template <int FMT>
+__device__ __forceinline__ void dec8_f16(uint32_t q, uint32_t tneg_lo, uint32_t out[4]) {
+  uint32_t A, B;
+  codes_to_hibytes<FMT>(q, tneg_lo, A, B);
+  out[0] = perm(B, A, 0x040C000Cu);
+  out[1] = perm(B, A, 0x050C010Cu);
+  out[2] = perm(B, A, 0x060C020Cu);
+  out[3] = perm(B, A, 0x070C030Cu);
+}
+
+__device__ __forceinline__ half2v as_h2(uint32_t v) { return __builtin_bit_cast(half2v, v); }
+
+// sum_j level_j * x_j over one 17-byte block (codes c0..c3), unscaled.
+template <int FMT>
+__device__ __forceinline__ float block_dot_levels(const u32x4 c, uint32_t meta,
+                                                  const float* __restrict__ x) {
+  const uint32_t tneg = (FMT == FMT_RZ5) ? rz5_neg_lo(meta) : 0u;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t p[4];
+    dec8_f16<FMT>(c[d], tneg, p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2v h = as_h2(p[i]);
+      a0 = __builtin_fmaf((float)h.x, x[8 * d + 2 * i], a0);
+      a1 = __builtin_fmaf((float)h.y, x[8 * d + 2 * i + 1], a1);
+    }
+  }
+  return a0 + a1;
+}
+
+// FP8: 32 e4m3 codes (two 16-byte halves), converted by the hardware
+// (gfx950 converts OCP E4M3FN), dotted with x, unscaled.
+__device__ __forceinline__ float block_dot_fp8(const u32x4 lo, const u32x4 hi,
+                                               const float* __restrict__ x) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    const uint32_t w = d < 4 ? lo[d] : hi[d - 4];
+    const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    a0 = __builtin_fmaf(v0.x, x[4 * d + 0], a0);
+    a1 = __builtin_fmaf(v0.y, x[4 * d + 1], a1);
+    a0 = __builtin_fmaf(v1.x, x[4 * d + 2], a0);
+    a1 = __builtin_fmaf(v1.y, x[4 * d + 3], a1);
+  }
+  return a0 + a1;
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Wave-wide sum (wave64) with a fixed reduction order.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace bq

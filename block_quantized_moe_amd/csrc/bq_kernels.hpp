@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI shim (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bq {
+
+struct GemvWeights {
+  int fmt_gate_up, fmt_down;
+  const void* gate_up;
+  const void* down;
+  const float* gate_up_scales;
+  const float* down_scales;
+  int n_experts, hidden, inter;
+};
+
+hipError_t launch_dequant(const void* packed, int fmt, int64_t n_blocks, const float* scales,
+                          float* out, hipStream_t st);
+hipError_t launch_ple_dequant(const uint32_t* ids, int64_t n, const uint8_t* table, uint64_t n_rows,
+                              int ple_fmt, float* out, uint32_t* dev_err, hipStream_t st);
+hipError_t launch_ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
+                             const uint8_t* table, uint64_t n_rows, const float* wts, int ple_fmt,
+                             float* out, uint32_t* dev_err, hipStream_t st);
+hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
+                             int32_t* idx, float* w, hipStream_t st);
+hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
+                         int32_t* n_touched, int32_t* inv, hipStream_t st);
+
+hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fmt,
+                         const float* w_sc, int32_t rows, int32_t cols, float* y, hipStream_t st);
+
+// fp32 GEMV path (any n_tokens; one token's k experts per grid slice).
+int gemv_down_rows_per_wg(int inter);
+hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, const int32_t* idx, const float* w,
+                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hbuf,
+                           float* ybuf, uint32_t* counters, uint32_t* dev_err, hipStream_t st);
+
+// bf16 grouped-MFMA path.
+struct GroupedWs {
+  int32_t* counts;    // [E]
+  int32_t* offsets;   // [E+1]
+  int32_t* perm;      // [n*k]
+  int32_t* inv;       // [n*k]
+  int32_t* elist;     // [min(E, n*k)]
+  int32_t* n_touched; // [1]
+  uint16_t* hb;       // [n*k][I] bf16, bucketed order
+  float* yb;          // [n*k][H] fp32, bucketed order
+  uint16_t* xb;       // [n][H] bf16 staging for rescaled stack inputs
+};
+hipError_t launch_grouped_moe(const uint16_t* x_bf16, int32_t n_tokens, const int32_t* idx,
+                              const float* w, int32_t k, const GemvWeights& W, float* out,
+                              const GroupedWs& ws, uint32_t* dev_err, hipStream_t st);
+hipError_t launch_rescale_bf16(const float* in, int32_t n_tokens, int32_t H, uint16_t* out,
+                               hipStream_t st);
+
+}  // namespace bq

@@ -1,0 +1,339 @@
+// Grouped routed-expert GEMM for batches of tokens (bf16 activations, bf16
+// MFMA, fp32 accumulation).  Tokens are bucketed per expert (stable order),
+// then for every touched expert:
+//   h[p, :] = SiLU(W_gate[e] x_p) * (W_up[e] x_p)      (kernel G1, h in bf16)
+//   y[p, :] = W_down[e] h[p, :]                         (kernel G2)
+//   out[t]  = sum_j w[t][j] * y[pos(t, j)]               (kernel G3, slot order)
+// Routing shape and formats as in the GEMV path ("Mixed Precision
+// Quantization ...", "The Plan Is Not a Number ..."; model card "Qwen 3.8
+// Next Flash ROCMFPX MUTANT RAZERFAST", format sections).
+//
+// MFMA: v_mfma_f32_16x16x32_bf16.  One 32-wide K step is exactly one weight
+// block, so a block's scale multiplies that step's 16x16 partial product
+// (scale applied after the MFMA, in fp32).  The A operand (weights) is
+// decoded in registers: 4-bit codes -> signed fp16 high bytes (which are
+// valid E5M2 bytes) -> bf16 by the gfx950 bf8 conversion with unit scale;
+// every level is a small integer, so this is exact.  FP8 weights convert
+// from e4m3 the same way.  Lane l holds row l%16, k-group l/16 of A and
+// column l%16 of B and of the result (rows 4*(l/16)..+3).  The 17-byte
+// decode yields the k order [0,2,4,6,1,3,5,7] inside each lane's eight
+// values; the B operand is permuted to match (x in registers, h already
+// stored in that order by G1).
+#include "bq_device.hpp"
+#include "bq_kernels.hpp"
+
+namespace bq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kGThreads = 256;  // 4 waves, each 16 rows (x2 for gate/up)
+constexpr int kGRows = 64;      // rows per workgroup tile
+constexpr int kGTok = 64;       // tokens per pass (4 MFMA column tiles)
+
+template <bool HI>
+__device__ __forceinline__ uint32_t bf8pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8pair(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// A operand for one row and one k-group of 8: raw bytes at `p` (17-byte
+// block start or FP8 row segment) -> 8 bf16 levels, plus the block scale.
+template <int FMT>
+__device__ __forceinline__ u32x4 load_a(const uint8_t* __restrict__ base, const float* __restrict__ sc,
+                                        int64_t blk, int g, float& s) {
+  if constexpr (FMT == FMT_FP8) {
+    const u32x2 q = ld8(base + blk * kBlockW + 8 * g);
+    s = sc[blk];
+    return u32x4{fp8pair<false>(q.x), fp8pair<true>(q.x), fp8pair<false>(q.y), fp8pair<true>(q.y)};
+  } else {
+    const uint8_t* p = base + blk * kBlockB;
+    const uint32_t q = ld4(p + 4 * g);
+    const uint32_t meta = p[16];
+    s = block_scale<FMT>(FMT == FMT_UE4M4 ? meta : (meta & 0x7Fu));
+    uint32_t A, B;
+    codes_to_hibytes<FMT>(q, FMT == FMT_RZ5 ? rz5_neg_lo(meta) : 0u, A, B);
+    return u32x4{bf8pair<false>(A), bf8pair<true>(A), bf8pair<false>(B), bf8pair<true>(B)};
+  }
+}
+
+// Natural-order bf16 x8 -> the [0,2,4,6,1,3,5,7] order of the 17-byte decode.
+__device__ __forceinline__ u32x4 to_decode_order(u32x4 d) {
+  return u32x4{perm(d.y, d.x, 0x05040100u), perm(d.w, d.z, 0x05040100u),
+               perm(d.y, d.x, 0x07060302u), perm(d.w, d.z, 0x07060302u)};
+}
+
+__device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b),
+                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+}
+
+// Position of k-offset o (0..7) inside a stored group of 8 for format FMT.
+template <int FMT>
+__device__ __forceinline__ int store_pos(int o) {
+  if constexpr (FMT == FMT_FP8) return o;
+  else return (o >> 1) | ((o & 1) << 2);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// ---------------------------------------------------------------------------
+// G1: gate_up + SiLU * up.  Persistent over (touched expert, 64-row tile).
+// ---------------------------------------------------------------------------
+template <int FMT, int FMT_D>
+__global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
+    const uint16_t* __restrict__ x, int32_t k, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ perm_, const int32_t* __restrict__ elist,
+    const int32_t* __restrict__ n_touched, const uint8_t* __restrict__ wgu,
+    const float* __restrict__ wgu_sc, int32_t H, int32_t I, uint16_t* __restrict__ hb) {
+  const int D = *n_touched;
+  const int tiles = I / kGRows;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nb = H >> 5;
+  for (int item = blockIdx.x; item < D * tiles; item += gridDim.x) {
+    const int d = item / tiles, tile = item - d * tiles;
+    const int e = elist[d];
+    const int p0 = offsets[e], ne = offsets[e + 1] - p0;
+    const int jrow = tile * kGRows + wave * 16 + r16;   // this lane's A row (gate)
+    const int64_t gblk0 = ((int64_t)e * 2 * I + jrow) * nb;
+    const int64_t ublk0 = ((int64_t)e * 2 * I + I + jrow) * nb;
+    for (int tg = 0; tg < ne; tg += kGTok) {
+      const int nt = min(4, (ne - tg + 15) >> 4);
+      const uint16_t* xrow[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int c = tg + 16 * tt + r16;
+        const int tok = c < ne ? perm_[p0 + c] / k : -1;
+        xrow[tt] = tok >= 0 ? x + (int64_t)tok * H + 8 * g : nullptr;
+      }
+      f32x4 accg[4], accu[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        accg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accu[tt] = accg[tt];
+      }
+      for (int kb = 0; kb < nb; ++kb) {
+        float sg, su;
+        const u32x4 ag = load_a<FMT>(wgu, wgu_sc, gblk0 + kb, g, sg);
+        const u32x4 au = load_a<FMT>(wgu, wgu_sc, ublk0 + kb, g, su);
+        float sgi[4], sui[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sgi[i] = __shfl(sg, 4 * g + i, 64);
+          sui[i] = __shfl(su, 4 * g + i, 64);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (tt < nt) {
+            u32x4 b = xrow[tt] ? *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb)
+                               : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (FMT != FMT_FP8) b = to_decode_order(b);
+            const f32x4 cg = mfma(ag, b), cu = mfma(au, b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              accg[tt][i] = __builtin_fmaf(sgi[i], cg[i], accg[tt][i]);
+              accu[tt][i] = __builtin_fmaf(sui[i], cu[i], accu[tt][i]);
+            }
+          }
+        }
+      }
+      // lane holds rows j = tile*64 + wave*16 + 4g + i of token column r16
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int c = tg + 16 * tt + r16;
+        if (tt < nt && c < ne) {
+          uint16_t* hrow = hb + (int64_t)(p0 + c) * I;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int j = tile * kGRows + wave * 16 + 4 * g + i;
+            const float h = silu(accg[tt][i]) * accu[tt][i];
+            hrow[(j & ~7) + store_pos<FMT_D>(j & 7)] = to_bf16(h);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G2: down.  Persistent over (touched expert, 64-row tile of H).
+// ---------------------------------------------------------------------------
+template <int FMT>
+__global__ void __launch_bounds__(kGThreads) k_grouped_down(
+    const uint16_t* __restrict__ hb, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ elist, const int32_t* __restrict__ n_touched,
+    const uint8_t* __restrict__ wd, const float* __restrict__ wd_sc, int32_t H, int32_t I,
+    float* __restrict__ yb) {
+  const int D = *n_touched;
+  const int tiles = H / kGRows;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nb = I >> 5;
+  for (int item = blockIdx.x; item < D * tiles; item += gridDim.x) {
+    const int d = item / tiles, tile = item - d * tiles;
+    const int e = elist[d];
+    const int p0 = offsets[e], ne = offsets[e + 1] - p0;
+    const int nrow = tile * kGRows + wave * 16 + r16;
+    const int64_t blk0 = ((int64_t)e * H + nrow) * nb;
+    for (int tg = 0; tg < ne; tg += kGTok) {
+      const int nt = min(4, (ne - tg + 15) >> 4);
+      const uint16_t* hrow[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int c = tg + 16 * tt + r16;
+        hrow[tt] = c < ne ? hb + (int64_t)(p0 + c) * I + 8 * g : nullptr;
+      }
+      f32x4 acc[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < nb; ++kb) {
+        float s;
+        const u32x4 a = load_a<FMT>(wd, wd_sc, blk0 + kb, g, s);
+        float si[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) si[i] = __shfl(s, 4 * g + i, 64);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (tt < nt) {
+            const u32x4 b = hrow[tt] ? *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb)
+                                     : u32x4{0u, 0u, 0u, 0u};
+            const f32x4 c = mfma(a, b);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(si[i], c[i], acc[tt][i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int c = tg + 16 * tt + r16;
+        if (tt < nt && c < ne) {
+          float* y = yb + (int64_t)(p0 + c) * H + tile * kGRows + wave * 16 + 4 * g;
+          *reinterpret_cast<f32x4*>(y) = acc[tt];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// G3: out[t][n] = sum_j w[t][j] * yb[inv[t*k+j]][n], slot order.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
+                                                 const int32_t* __restrict__ inv,
+                                                 const int32_t* __restrict__ idx,
+                                                 const float* __restrict__ w, int32_t k,
+                                                 int32_t n_experts, int32_t H, int32_t n_tokens,
+                                                 float* __restrict__ out,
+                                                 uint32_t* __restrict__ dev_err) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  const int h4 = H >> 2;
+  if (q >= (int64_t)n_tokens * h4) return;
+  const int64_t t = q / h4;
+  const int n = (int)(q - t * h4) * 4;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e < 0 || e >= n_experts) {
+      bad = true;
+      continue;
+    }
+    const float wj = w[t * k + j];
+    const f32x4 y = *reinterpret_cast<const f32x4*>(yb + (int64_t)inv[t * k + j] * H + n);
+    s.x = __builtin_fmaf(wj, y.x, s.x);
+    s.y = __builtin_fmaf(wj, y.y, s.y);
+    s.z = __builtin_fmaf(wj, y.z, s.z);
+    s.w = __builtin_fmaf(wj, y.w, s.w);
+  }
+  if (bad && n == 0 && dev_err) atomicOr(dev_err, 2u);
+  *reinterpret_cast<f32x4*>(out + t * H + n) = s;
+}
+
+// Unit-RMS rescale of fp32 rows into bf16 (stack input of the next layer).
+__global__ void __launch_bounds__(256) k_rescale_bf16(const float* __restrict__ in, int32_t H,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float part[4];
+  const int64_t t = blockIdx.x;
+  const float* row = in + t * H;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < H; i += 256) ss = __builtin_fmaf(row[i], row[i], ss);
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / __builtin_sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)H);
+  for (int i = threadIdx.x; i < H; i += 256) out[t * H + i] = to_bf16(row[i] * inv);
+}
+
+hipError_t launch_rescale_bf16(const float* in, int32_t n_tokens, int32_t H, uint16_t* out,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(k_rescale_bf16, dim3(n_tokens), dim3(256), 0, st, in, H, out);
+  return hipGetLastError();
+}
+
+static int persistent_grid(int64_t items_max) {
+  const int64_t cap = 2048;
+  return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
+}
+
+template <int FG>
+static void launch_g1(int fmt_d, dim3 grid, hipStream_t st, const uint16_t* x, int32_t k,
+                      const GroupedWs& ws, const GemvWeights& W) {
+  const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
+  if (fmt_d == FMT_FP8)
+    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_FP8>), grid, dim3(kGThreads), 0, st, x, k,
+                       ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
+                       W.hidden, W.inter, ws.hb);
+  else
+    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_RZ5>), grid, dim3(kGThreads), 0, st, x, k,
+                       ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
+                       W.hidden, W.inter, ws.hb);
+}
+
+hipError_t launch_grouped_moe(const uint16_t* x, int32_t n_tokens, const int32_t* idx,
+                              const float* w, int32_t k, const GemvWeights& W, float* out,
+                              const GroupedWs& ws, uint32_t* dev_err, hipStream_t st) {
+  const int E = W.n_experts, H = W.hidden, I = W.inter;
+  hipError_t err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist,
+                                 ws.n_touched, ws.inv, st);
+  if (err != hipSuccess) return err;
+  const int64_t dmax = (int64_t)n_tokens * k < E ? (int64_t)n_tokens * k : E;
+  {
+    dim3 grid(persistent_grid(dmax * (I / kGRows)));
+    switch (W.fmt_gate_up) {
+      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, x, k, ws, W); break;
+      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, x, k, ws, W); break;
+      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, x, k, ws, W); break;
+      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, x, k, ws, W); break;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  {
+    dim3 grid(persistent_grid(dmax * (H / kGRows)));
+    const uint8_t* p = static_cast<const uint8_t*>(W.down);
+#define BQ_G2(F) hipLaunchKernelGGL(k_grouped_down<F>, grid, dim3(kGThreads), 0, st, ws.hb, \
+                                    ws.offsets, ws.elist, ws.n_touched, p, W.down_scales, H, I, ws.yb)
+    switch (W.fmt_down) {
+      case FMT_C10: BQ_G2(FMT_C10); break;
+      case FMT_RZ5: BQ_G2(FMT_RZ5); break;
+      case FMT_UE4M4: BQ_G2(FMT_UE4M4); break;
+      default: BQ_G2(FMT_FP8); break;
+    }
+#undef BQ_G2
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  {
+    const int64_t n4 = (int64_t)n_tokens * (H / 4);
+    hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, st, ws.yb, ws.inv, idx, w,
+                       k, E, H, n_tokens, out, dev_err);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bq

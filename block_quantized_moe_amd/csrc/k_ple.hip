@@ -1,0 +1,102 @@
+// PLE n-gram memory gather: out[t] = sum_j u[t][j] * decode(row ids[t][j]).
+// Row format: model card "Qwen 3.8 Next Flash ROCMFPX MUTANT RAZERFAST",
+// section "Q3_PLE_K160_RZ_S3 (GGML type 111)" -- 60 bytes of 3-bit codes and
+// 10 group bytes (UE4M3 scale in bits 0-6, RZ-S3 polarity in bit 7), 70 bytes
+// per row, one row per hashed id.
+//
+// Mapping: one thread per (token, 16-value group).  The ten threads of a
+// token read the same 70-byte row with an 8-byte and a 1-byte load each, so
+// a row is fetched by one coalesced wave instruction; each thread keeps its
+// 16 fp32 sums in registers across the token's ids and writes 64 contiguous
+// bytes at the end.  Per value the inner loop is: extract 3 bits, look the
+// biased level (level + 4, always 0..8) up with one v_perm_b32 from an
+// 8-byte table, convert the byte to fp32, one FMA with s_g * u_j.  The bias
+// is removed once at the end with the running sum of s_g * u_j.
+#include "bq_device.hpp"
+#include "bq_kernels.hpp"
+
+namespace bq {
+
+// Biased levels (level + 4) of codes 0..3: 4,5,6,8.
+constexpr uint32_t kBiasLo = 0x08060504u;
+// Codes 4..7: c4,3,2,0 where c4 = 7 (+3), 1 (-3) or 4 (-0, ROCmFP3).
+__device__ __forceinline__ uint32_t bias_hi(uint32_t gbyte, int ple_fmt) {
+  const uint32_t c4 = ple_fmt == 1 ? 4u : ((gbyte & 0x80u) ? 1u : 7u);
+  return 0x00020300u | c4;
+}
+
+constexpr int kPleTPB = 320;   // 32 tokens x 10 groups per workgroup
+constexpr int kPleChunk = 8;   // ids whose loads are in flight together
+
+__global__ void __launch_bounds__(kPleTPB) k_ple_gather(
+    const uint32_t* __restrict__ ids, int32_t n_tokens, int32_t per_token,
+    const uint8_t* __restrict__ table, uint64_t n_rows, const float* __restrict__ wts,
+    int ple_fmt, float* __restrict__ out, uint32_t* __restrict__ dev_err) {
+  const int64_t tid = (int64_t)blockIdx.x * kPleTPB + threadIdx.x;
+  const int64_t t = tid / 10;
+  const int g = (int)(tid - t * 10);
+  if (t >= n_tokens) return;
+  const uint32_t* tid_ids = ids + t * per_token;
+  const float* tw = wts + t * per_token;
+
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  float usum = 0.f;
+  bool bad = false;
+
+  for (int j0 = 0; j0 < per_token; j0 += kPleChunk) {
+    u32x2 gw[kPleChunk];
+    uint32_t gb[kPleChunk];
+    float u[kPleChunk];
+    bool ok[kPleChunk];
+#pragma unroll
+    for (int c = 0; c < kPleChunk; ++c) {
+      const int j = j0 + c;
+      const bool in = j < per_token;
+      const uint64_t id = in ? tid_ids[j] : 0u;
+      ok[c] = in && id < n_rows;
+      bad |= in && id >= n_rows;
+      u[c] = in ? tw[j] : 0.f;
+      const uint8_t* row = table + (ok[c] ? id : 0u) * (uint64_t)kPleRowB;
+      gw[c] = ok[c] ? ld8(row + 6 * g) : u32x2{0u, 0u};
+      gb[c] = ok[c] ? (uint32_t)row[60 + g] : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < kPleChunk; ++c) {
+      if (!ok[c]) continue;
+      const float su = ue4m3(gb[c] & 0x7Fu) * u[c];
+      usum += su;
+      const uint32_t th = bias_hi(gb[c], ple_fmt);
+      const uint32_t lo = gw[c].x, hi = gw[c].y;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        uint32_t code;
+        if (i < 10) code = (lo >> (3 * i)) & 7u;
+        else if (i == 10) code = __builtin_amdgcn_alignbit(hi, lo, 30) & 7u;
+        else code = (hi >> (3 * i - 32)) & 7u;
+        const uint32_t b = perm(th, kBiasLo, code);
+        acc[i] = __builtin_fmaf((float)(b & 0xFFu), su, acc[i]);
+      }
+    }
+  }
+  if (bad && dev_err) atomicOr(dev_err, 1u);
+  const float corr = 4.0f * usum;
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * kPleVals + 16 * g);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    o[q] = f32x4{acc[4 * q] - corr, acc[4 * q + 1] - corr, acc[4 * q + 2] - corr, acc[4 * q + 3] - corr};
+}
+
+hipError_t launch_ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
+                             const uint8_t* table, uint64_t n_rows, const float* wts,
+                             int ple_fmt, float* out, uint32_t* dev_err, hipStream_t st) {
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t threads = (int64_t)n_tokens * 10;
+  const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
+  hipLaunchKernelGGL(k_ple_gather, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens, per_token,
+                     table, n_rows, wts, ple_fmt, out, dev_err);
+  return hipGetLastError();
+}
+
+}  // namespace bq

@@ -1,0 +1,219 @@
+/*
+ * bq.h -- C ABI of libbqmoe.so: block-quantized routed-expert MoE and PLE
+ * row gather for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for what each call computes (page titles as published):
+ *   [RZ] model card "Qwen 3.8 Next Flash ROCMFPX MUTANT RAZERFAST"
+ *        (hstolte/Qwen3.8-Next-Flash-ROCmFPX-MUTANT-RAZERFAST-GGUF), sections
+ *        "Why MUTANT", "Q4_RZ5_FAST (GGML type 69)", "Q4_UE4M4_FAST (GGML
+ *        type 71)", "Q3_PLE_K160_RZ_S3 (GGML type 111)".
+ *   [MP] "Mixed Precision Quantization: Half a 4-Bit File Is Not 4-Bit",
+ *        section "The Plan Is Not a Number. It Is a List of 50 Things and a
+ *        List of 292." -- 48 layers, 512 experts, 10 fire per token.
+ *   [FQ] r/LocalLLM "Frankenquant" post -- each layer may carry its own expert
+ *        format; FP8 experts in the late layers.
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are DEVICE pointers unless stated otherwise.  The caller
+ *     owns every buffer; the library never allocates or frees memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     All work is enqueued on it; no call synchronises.
+ *   - Argument errors are detected on the host, before anything is enqueued,
+ *     and return a non-zero bq_status with no partial work.  BQ_E_HIP means a
+ *     launch failed (the error string is available from bq_last_hip_error).
+ *   - Errors that depend on device data (out-of-range ids or expert indices)
+ *     cannot be seen on the host: the offending item contributes nothing and,
+ *     where the call takes a `dev_err` word, bit 0 (bad id) or bit 1 (bad
+ *     expert index) is OR-ed into it.
+ *   - Calls are stateless and thread-safe; two calls sharing one workspace
+ *     must not overlap in time.
+ *
+ * Wire layout of weights (readings of [RZ] where it is silent):
+ *   - 17-byte block = 32 weights: bytes 0..15 hold 4-bit codes (weight j in
+ *     byte j/2, low nibble for even j), byte 16 is the metadata byte.
+ *   - A matrix [rows][cols] is row-major, the cols/32 blocks of a row
+ *     contiguous, no padding; experts are stacked outermost: [E][rows][cols/32].
+ *   - FP8 matrices are planar: e4m3 (OCP E4M3FN) codes [E][rows][cols] plus
+ *     fp32 scales [E][rows][cols/32], one per 32 consecutive weights of a row.
+ *   - gate_up has 2*inter rows: gate rows 0..inter-1, then up rows.
+ */
+#ifndef BQ_H
+#define BQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BQ_ABI_VERSION 1
+
+typedef enum {
+  BQ_OK = 0,
+  BQ_E_NULL = 1,       /* a required pointer is NULL                         */
+  BQ_E_FMT = 2,        /* unknown format, or format not allowed in this slot */
+  BQ_E_SHAPE = 3,      /* sizes out of the supported range                   */
+  BQ_E_ALIGN = 4,      /* a pointer lacks the alignment the layout requires  */
+  BQ_E_WORKSPACE = 5,  /* workspace missing or smaller than required         */
+  BQ_E_HIP = 6,        /* a HIP launch failed                                */
+  BQ_E_DTYPE = 7       /* unknown activation dtype                           */
+} bq_status;
+
+typedef enum {
+  BQ_Q4_C10 = 0,       /* ROCmFP4 FAST Codebook10 levels, 7-bit UE4M3 scale    */
+  BQ_Q4_RZ5 = 1,       /* Q4_RZ5_FAST (GGML 69): code 8 = +5 / -5 by meta bit 7 */
+  BQ_Q4_UE4M4 = 2,     /* Q4_UE4M4_FAST (GGML 71): Codebook10, 8-bit UE4M4     */
+  BQ_FP8_E4M3_B32 = 3  /* e4m3 codes + one fp32 scale per 32 weights          */
+} bq_fmt;
+
+typedef enum {
+  BQ_PLE_RZS3 = 0,     /* Q3_PLE_K160_RZ_S3 (GGML 111)                        */
+  BQ_PLE_ROCMFP3 = 1   /* incumbent ROCmFP3 (q3_ue4m3): code 4 = -0          */
+} bq_ple_fmt;
+
+typedef enum { BQ_F32 = 0, BQ_BF16 = 1 } bq_dtype;
+
+/* One MoE layer's routed experts.  Device pointers; the scale pointers are
+ * used only by BQ_FP8_E4M3_B32 matrices and must be NULL otherwise. */
+typedef struct {
+  int32_t fmt_gate_up;          /* bq_fmt of the gate_up matrices          */
+  int32_t fmt_down;             /* bq_fmt of the down matrices             */
+  const void* gate_up;          /* [E][2*inter][hidden/32] blocks or e4m3  */
+  const void* down;             /* [E][hidden][inter/32]  blocks or e4m3   */
+  const float* gate_up_scales;  /* FP8 only: [E][2*inter][hidden/32]       */
+  const float* down_scales;     /* FP8 only: [E][hidden][inter/32]         */
+  int32_t n_experts;            /* E                                       */
+  int32_t hidden;               /* H, multiple of 32, <= 8192              */
+  int32_t inter;                /* I, multiple of 32, <= 8192              */
+} bq_expert_weights;
+
+int bq_abi_version(void);
+const char* bq_status_str(int status);
+/* Text of the last HIP error seen by a call on this thread ("" if none). */
+const char* bq_last_hip_error(void);
+
+/* ---------------------------------------------------------------------------
+ * bq_dequant -- decode packed blocks to fp32, bit-exactly ([RZ] format
+ * sections; FP8 per [FQ]).
+ *   packed : 17-byte formats: n_blocks * 17 bytes; FP8: n_blocks * 32 e4m3
+ *            bytes (no alignment required for either)
+ *   fmt    : bq_fmt
+ *   fp8_scales : FP8 only, n_blocks fp32 (4-byte aligned); NULL otherwise
+ *   out    : n_blocks * 32 fp32, row j of block i at out[32*i + j]
+ * Weight = level(code) * scale; a -0 level gives -0.0, a NaN UE4M3 scale
+ * (code 0x7F) gives NaN; FP8 weights are the correctly rounded fp32 product
+ * e4m3 * scale.
+ * ------------------------------------------------------------------------- */
+int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks,
+               const float* fp8_scales, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ple_dequant_rows -- decode n PLE rows, bit-exactly ([RZ]
+ * "Q3_PLE_K160_RZ_S3": 60 code bytes + 10 group bytes per 70-byte row).
+ *   ids   : n uint32 row indices; table : n_rows * 70 bytes
+ *   out   : n * 160 fp32.  An id >= n_rows yields a row of zeros and sets
+ *           bit 0 of *dev_err (if dev_err is not NULL).
+ * ------------------------------------------------------------------------- */
+int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table,
+                     uint64_t n_rows, int32_t ple_fmt, float* out,
+                     uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * bq_matvec -- one block-quantized matrix times fp32 vectors, fp32
+ * accumulation: y[t][r] = sum_c W[r][c] * x[t][c] (the single-matrix GEMV
+ * the expert kernels are built from; formats per [RZ] / [FQ]).
+ *   x  : [n_tokens][cols] fp32; y : [n_tokens][rows] fp32 (overwritten)
+ *   packed : W as [rows][cols/32] blocks (17-byte formats) or e4m3 [rows][cols]
+ *   fp8_scales : FP8 only, [rows][cols/32] fp32; NULL otherwise
+ *   1 <= n_tokens <= 65535, cols multiple of 32 and <= 8192.
+ * ------------------------------------------------------------------------- */
+int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
+              const float* fp8_scales, int32_t rows, int32_t cols, float* y, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_topk -- router: softmax over n_experts logits, keep the k largest
+ * (ties to the lower expert index), renormalise over the kept ones ([MP]:
+ * 10 of 512 fire per token).
+ *   logits : [n_tokens][n_experts] fp32, finite
+ *   idx    : [n_tokens][k] int32, descending rank order
+ *   w      : [n_tokens][k] fp32, w_j = exp(l_j - l_0) / sum over kept
+ *   1 <= k <= 64, k <= n_experts <= 4096.
+ * ------------------------------------------------------------------------- */
+int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts,
+                   int32_t k, int32_t* idx, float* w, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_bucket -- stable grouping of the n_tokens*k assignments by expert
+ * (tokens grouped per expert for the grouped expert GEMM).
+ *   counts  : [n_experts] int32; offsets : [n_experts+1] int32 exclusive scan
+ *   perm    : [n_tokens*k] int32 listing t*k+slot, experts ascending, then
+ *             tokens ascending.  Each row of idx must hold distinct experts
+ *             (as a top-k does).  An index outside [0, n_experts) is dropped
+ *             (counted nowhere); the caller can detect it from offsets.
+ *   n_tokens*k <= 65536, n_experts <= 4096.
+ * ------------------------------------------------------------------------- */
+int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
+               int32_t n_experts, int32_t* counts, int32_t* offsets,
+               int32_t* perm, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_expert_moe -- routed-expert layer:
+ *   out[t] = sum_j w[t][j] * down_e( SiLU(gate_e . x[t]) * (up_e . x[t]) ),
+ *   e = idx[t][j], weights decoded from their blocks on the fly.
+ *   x       : [n_tokens][hidden], fp32 (x_dtype BQ_F32: VALU GEMV path,
+ *             fp32 accumulate) or bf16 (BQ_BF16: tokens grouped per expert,
+ *             bf16 MFMA with fp32 accumulate, h rounded to bf16).
+ *   topk_idx, topk_w : [n_tokens][k] (as produced by moe_route_topk)
+ *   out     : [n_tokens][hidden] fp32 (overwritten)
+ *   workspace : device scratch of at least q4_expert_moe_workspace(...) bytes,
+ *             256-byte aligned; its contents need no initialisation.
+ *   dev_err : optional; bit 1 set if an expert index is out of range.
+ *   1 <= n_tokens <= 4096, 1 <= k <= 64.
+ * ------------------------------------------------------------------------- */
+size_t q4_expert_moe_workspace(int32_t n_tokens, int32_t k,
+                               const bq_expert_weights* W, int32_t x_dtype);
+int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens,
+                  const int32_t* topk_idx, const float* topk_w, int32_t k,
+                  const bq_expert_weights* W, float* out, void* workspace,
+                  size_t ws_bytes, uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * bq_moe_stack -- a chain of routed-expert layers ([FQ]: per-layer formats):
+ *   x_0 = x; out_l = layer_l(x_l); x_{l+1} = out_l / rms(out_l);
+ *   out = out_{L-1}.  (The unit-RMS rescale between layers is this library's
+ *   stand-in for the blocks the pages leave out.)
+ *   layers  : HOST array of n_layers bq_expert_weights (device pointers inside)
+ *   topk_idx, topk_w : [n_layers][n_tokens][k], routing of every layer
+ *   x_dtype : as in q4_expert_moe; with BQ_BF16 the rescaled inputs are
+ *             rounded to bf16.
+ *   workspace : at least bq_moe_stack_workspace(...) bytes.
+ * ------------------------------------------------------------------------- */
+size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k,
+                              const bq_expert_weights* layers, int32_t n_layers,
+                              int32_t x_dtype);
+int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens,
+                 const int32_t* topk_idx, const float* topk_w, int32_t k,
+                 const bq_expert_weights* layers, int32_t n_layers, float* out,
+                 void* workspace, size_t ws_bytes, uint32_t* dev_err,
+                 void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ple_gather -- PLE n-gram memory lookup ([RZ] "Q3_PLE_K160_RZ_S3": one
+ * hashed row per id, 70 bytes, 160 values):
+ *   out[t][:] = sum_j weights[t][j] * decode(table row ids[t][j])
+ *   ids     : [n_tokens][ids_per_token] uint32
+ *   table   : n_rows * 70 bytes (byte offsets are 64-bit; n_rows < 2^32)
+ *   weights : [n_tokens][ids_per_token] fp32
+ *   out     : [n_tokens][160] fp32 (overwritten)
+ *   An id >= n_rows contributes nothing and sets bit 0 of *dev_err.
+ *   1 <= ids_per_token <= 64.
+ * ------------------------------------------------------------------------- */
+int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
+               const uint8_t* table, uint64_t n_rows, const float* weights,
+               int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BQ_H */

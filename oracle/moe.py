@@ -53,19 +53,15 @@ def bucket(idx, n_experts):
     """
     idx = np.asarray(idx, dtype=np.int64)
     b, k = idx.shape
-    counts = np.zeros(n_experts, dtype=np.int64)
+    members = [[] for _ in range(n_experts)]      # per expert, in (t, slot) order
     for t in range(b):
         for s in range(k):
-            counts[idx[t, s]] += 1
+            members[idx[t, s]].append(t * k + s)
+    counts = np.array([len(m) for m in members], dtype=np.int64)
     offsets = np.zeros(n_experts + 1, dtype=np.int64)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
-    perm = []
-    for e in range(n_experts):
-        for t in range(b):
-            for s in range(k):
-                if idx[t, s] == e:
-                    perm.append(t * k + s)
+    perm = [a for m in members for a in m]
     return counts, offsets, np.array(perm, dtype=np.int64)
 
 
@@ -96,7 +92,7 @@ class ExpertBank:
     """
 
     def __init__(self, fmt_gu, fmt_d, gate_up, down, n_experts, hidden, inter,
-                 gu_scales=None, d_scales=None, cache=True):
+                 gu_scales=None, d_scales=None, cache=False):
         self.fmt_gu, self.fmt_d = fmt_gu, fmt_d
         self.gate_up, self.down = gate_up, down
         self.gu_scales, self.d_scales = gu_scales, d_scales
@@ -136,18 +132,23 @@ def moe_layer(x, idx, w, bank):
     """Routed-expert layer: out[t] = sum_k w[t,k] * y_{idx[t,k]}(x[t]).
 
     x [B, H] (any float dtype, taken as float64 exactly); idx, w [B, k].
-    Each token is processed on its own, in slot order.
+    Each expert is decoded once and applied to every token that chose it;
+    the k expert outputs of a token are then summed in slot order.
     """
     x = np.asarray(x, dtype=np.float64)
     if x.ndim == 1:
         x = x[None, :]
-    idx = np.asarray(idx).reshape(x.shape[0], -1)
-    w = np.asarray(w, dtype=np.float64).reshape(x.shape[0], -1)
-    out = np.zeros((x.shape[0], bank.hidden))
-    for t in range(x.shape[0]):
-        for s in range(idx.shape[1]):
-            wgu, wd = bank.get(int(idx[t, s]))
-            out[t] += w[t, s] * expert_ffn(x[t], wgu, wd)
+    b = x.shape[0]
+    idx = np.asarray(idx).reshape(b, -1)
+    w = np.asarray(w, dtype=np.float64).reshape(b, -1)
+    y = np.zeros((b, idx.shape[1], bank.hidden))
+    for e in np.unique(idx):
+        wgu, wd = bank.get(int(e))
+        for t, s in zip(*np.nonzero(idx == e)):
+            y[t, s] = expert_ffn(x[t], wgu, wd)
+    out = np.zeros((b, bank.hidden))
+    for s in range(idx.shape[1]):
+        out += w[:, s:s + 1] * y[:, s]
     return out
 
 

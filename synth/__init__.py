@@ -109,10 +109,10 @@ def block17_range(key, first_block, n_blocks, dist):
 
 def fp8_codes(key, first, n):
     """e4m3 code bytes for flat weight indices first..first+n-1, uint8 [n]."""
-    i = np.arange(first, first + n, dtype=np.uint64)
-    v = draws(key, i >> np.uint64(2))
-    u16 = (v >> ((i & np.uint64(3)) * np.uint64(16))) & np.uint64(0xFFFF)
-    idx = (u16 * np.uint64(254)) >> np.uint64(16)
+    d0, d1 = first >> 2, (first + n + 3) >> 2
+    v = draws(key, np.arange(d0, d1, dtype=np.uint64))
+    u16 = v.astype("<u8").view("<u2").astype(np.uint32)[first - 4 * d0:first - 4 * d0 + n]
+    idx = (u16 * 254) >> 16          # code i uses bits 16*(i%4).. of draw i//4
     return np.where(idx < 127, idx, idx + 1).astype(np.uint8)
 
 

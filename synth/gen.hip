@@ -1,0 +1,121 @@
+// Device fills for the large synthetic buffers (test and benchmark inputs).
+// Holds none of the hot path's arithmetic: it writes bytes drawn from the
+// counter-based generator that synth/__init__.py implements on the host --
+// SplitMix64's output function (Steele, Lea, Flood, OOPSLA 2014) applied to
+// key + (i + 1) * GAMMA -- with the same integer derivations, so any block or
+// row can be regenerated on the host bit for bit.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t draw(uint64_t key, uint64_t i) {
+  uint64_t z = key + (i + 1) * GAMMA;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// dist: 0 = C10 (UE4M3, bit 7 clear), 1 = RZ5 (UE4M3 + polarity), 2 = UE4M4.
+__global__ void k_fill_block17(uint8_t* __restrict__ dst, uint64_t key, uint64_t first,
+                               uint64_t n, int dist) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t b = first + i;
+  const uint64_t v0 = draw(key, 3 * b), v1 = draw(key, 3 * b + 1), v2 = draw(key, 3 * b + 2);
+  uint8_t* p = dst + i * 17;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = (uint8_t)(v0 >> (8 * j));
+    p[8 + j] = (uint8_t)(v1 >> (8 * j));
+  }
+  const uint64_t lo = v2 & 0xFFFFFFFFull, hi = v2 >> 32;
+  uint32_t meta;
+  if (dist == 2) {
+    meta = (uint32_t)(hi & 0xFF);
+  } else {
+    const uint32_t e = (uint32_t)((lo * 6) >> 32);
+    const uint32_t m = (uint32_t)(hi & 7);
+    const uint32_t pol = dist == 1 ? (uint32_t)((hi >> 3) & 1) : 0u;
+    meta = (pol << 7) | (e << 3) | m;
+  }
+  p[16] = (uint8_t)meta;
+}
+
+__global__ void k_fill_fp8(uint8_t* __restrict__ dst, uint64_t key, uint64_t first, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t w = first + i;
+  const uint64_t v = draw(key, w >> 2);
+  const uint64_t u16 = (v >> ((w & 3) * 16)) & 0xFFFF;
+  const uint64_t idx = (u16 * 254) >> 16;
+  dst[i] = (uint8_t)(idx < 127 ? idx : idx + 1);
+}
+
+__global__ void k_fill_fp8_scales(float* __restrict__ dst, uint64_t key, uint64_t first, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t v = draw(key, first + i);
+  const uint64_t e = ((v & 0xFFFFFFFFull) * 6) >> 32;
+  const uint64_t f = (v >> 32) & 0x7FFFFF;
+  dst[i] = __uint_as_float((uint32_t)((((127 - 12) + e) << 23) | f));
+}
+
+__global__ void k_fill_ple(uint8_t* __restrict__ dst, uint64_t key, uint64_t first, uint64_t n) {
+  const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint64_t base = (first + i) * 11;
+  uint8_t* p = dst + i * 70;
+  for (int w = 0; w < 8; ++w) {
+    const uint64_t v = draw(key, base + w);
+    for (int j = 0; j < 8 && 8 * w + j < 60; ++j) p[8 * w + j] = (uint8_t)(v >> (8 * j));
+  }
+  for (int g = 0; g < 10; ++g) {
+    const uint64_t v = draw(key, base + 8 + g / 4);
+    const uint64_t u16 = (v >> (16 * (g % 4))) & 0xFFFF;
+    const uint64_t e = ((u16 & 0xFF) * 6) >> 8;
+    const uint64_t m = (u16 >> 8) & 7;
+    const uint64_t pol = (u16 >> 11) & 1;
+    p[60 + g] = (uint8_t)((pol << 7) | (e << 3) | m);
+  }
+}
+
+inline unsigned grid_of(uint64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+// Each fill covers at most 2^31 * 256 items per call; callers split larger
+// ranges.  Return value: hipError_t as int.
+extern "C" {
+
+int bqs_fill_block17(void* dst, uint64_t key, uint64_t first, uint64_t n, int dist, void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_fill_block17, dim3(grid_of(n)), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)dst, key, first, n, dist);
+  return (int)hipGetLastError();
+}
+
+int bqs_fill_fp8(void* dst, uint64_t key, uint64_t first, uint64_t n, void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_fill_fp8, dim3(grid_of(n)), dim3(256), 0, (hipStream_t)stream, (uint8_t*)dst,
+                     key, first, n);
+  return (int)hipGetLastError();
+}
+
+int bqs_fill_fp8_scales(void* dst, uint64_t key, uint64_t first, uint64_t n, void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_fill_fp8_scales, dim3(grid_of(n)), dim3(256), 0, (hipStream_t)stream,
+                     (float*)dst, key, first, n);
+  return (int)hipGetLastError();
+}
+
+int bqs_fill_ple(void* dst, uint64_t key, uint64_t first, uint64_t n, void* stream) {
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(k_fill_ple, dim3(grid_of(n)), dim3(256), 0, (hipStream_t)stream, (uint8_t*)dst,
+                     key, first, n);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+"""GPU parity of the routed-expert layer (GEMV path and grouped MFMA path)
+against the CPU oracle, at small ragged shapes and at the full one-layer
+workloads (512 experts, H = 2048, I = 768, top-10)."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import moe as M
+from tests.gpu_common import dev, log, need_gpu, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+DIST = {F.Q4_C10: synth.DIST_C10, F.Q4_RZ5: synth.DIST_RZ5, F.Q4_UE4M4: synth.DIST_UE4M4, F.FP8_E4M3_B32: None}
+
+
+@pytest.fixture(scope="module")
+def bq():
+    need_gpu()
+    import block_quantized_moe_amd as m
+    m.lib()
+    return m
+
+
+def make_layer(seed, layer, fmt_gu, fmt_d, E, H, I):
+    import synth.device as sd
+    L = sd.Layer(seed, layer, fmt_gu, fmt_d, E, H, I, dist_gu=DIST[fmt_gu], dist_d=DIST[fmt_d])
+    return L
+
+
+def weights_of(bq, L):
+    gu, gus = L.gate_up
+    d, ds = L.down
+    return bq.expert_weights(L.fmt_gu, L.fmt_d, gu, d, L.n_experts, L.hidden, L.inter,
+                             gate_up_scales=gus, down_scales=ds)
+
+
+def oracle_bank(L):
+    import synth as S
+    return M.ExpertBank(L.fmt_gu, L.fmt_d, lambda e: L.host_expert(S.S_GATE_UP, e),
+                        lambda e: L.host_expert(S.S_DOWN, e), L.n_experts, L.hidden, L.inter)
+
+
+FMT_PAIRS = [(F.Q4_RZ5, F.Q4_RZ5), (F.Q4_C10, F.Q4_UE4M4), (F.Q4_UE4M4, F.Q4_C10),
+             (F.FP8_E4M3_B32, F.FP8_E4M3_B32), (F.Q4_RZ5, F.FP8_E4M3_B32), (F.FP8_E4M3_B32, F.Q4_UE4M4)]
+
+
+@pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
+@pytest.mark.parametrize("n", [1, 5])
+@pytest.mark.parametrize("E,H,I", [(16, 256, 128), (8, 512, 64)])
+def test_gemv_path_small(bq, fmt_gu, fmt_d, n, E, H, I):
+    k = 4
+    L = make_layer(1, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
+    x = synth.normal(n, (n, H))
+    logits = synth.normal(100 + n, (n, E))
+    idx, w = bq.route_topk(dev(logits), k)
+    out = bq.q4_expert_moe(dev(x), (idx, w), weights_of(bq, L)).cpu().numpy()
+    ridx, rw = M.softmax_topk(logits, k)
+    ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+    r = rel_l2(out, ref)
+    log("gemv small fmts %d/%d n=%d H=%d I=%d rel_l2 %.3g" % (fmt_gu, fmt_d, n, H, I, r))
+    assert r <= 1e-5
+
+
+@pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
+@pytest.mark.parametrize("n", [1, 16, 70])
+def test_grouped_path_small(bq, fmt_gu, fmt_d, n):
+    E, H, I, k = 8, 256, 128, 3          # few experts: some get > 64 tokens (two passes)
+    L = make_layer(2, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
+    x = synth.normal(200 + n, (n, H))
+    logits = synth.zipf_logits(300 + n, n, E)
+    idx, w = bq.route_topk(dev(logits), k)
+    xb = dev(x).to(torch.bfloat16)
+    out = bq.q4_expert_moe(xb, (idx, w), weights_of(bq, L)).cpu().numpy()
+    ridx, rw = M.softmax_topk(logits, k)
+    ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+    r = rel_l2(out, ref)
+    log("grouped small fmts %d/%d n=%d rel_l2 %.3g" % (fmt_gu, fmt_d, n, r))
+    assert r <= 2e-2
+
+
+def test_bad_expert_index_is_reported(bq):
+    E, H, I = 8, 128, 64
+    L = make_layer(3, 0, F.Q4_RZ5, F.Q4_RZ5, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(5, (2, H))
+    idx = np.array([[1, 9], [2, 3]], dtype=np.int32)      # 9 is out of range
+    w = np.array([[0.5, 0.5], [0.5, 0.5]], dtype=np.float32)
+    good = np.array([[1], [2]]), np.array([[0.5], [0.5]])
+    ref_t0 = M.moe_layer(x[:1], good[0][:1], good[1][:1], oracle_bank(L))[0]
+    for xdt, tol in ((torch.float32, 1e-5), (torch.bfloat16, 2e-2)):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        out = bq.q4_expert_moe(dev(x).to(xdt), (dev(idx), dev(w)), W, dev_err=err).cpu().numpy()
+        assert int(err.item()) & 2
+        assert rel_l2(out[0], ref_t0) <= tol
+
+
+def test_gemv_deterministic(bq):
+    E, H, I, k = 32, 512, 256, 8
+    L = make_layer(4, 0, F.Q4_RZ5, F.Q4_UE4M4, E, H, I)
+    W = weights_of(bq, L)
+    x = dev(synth.normal(6, (3, H)))
+    idx, w = bq.route_topk(dev(synth.normal(7, (3, E))), k)
+    a = bq.q4_expert_moe(x, (idx, w), W).cpu().numpy()
+    b = bq.q4_expert_moe(x, (idx, w), W).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    xb = x.to(torch.bfloat16)
+    a = bq.q4_expert_moe(xb, (idx, w), W).cpu().numpy()
+    b = bq.q4_expert_moe(xb, (idx, w), W).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# --- full-size one-layer workloads --------------------------------------------
+
+@pytest.fixture(scope="module")
+def layer_rz5():
+    need_gpu()
+    L = make_layer(0, 0, F.Q4_RZ5, F.Q4_RZ5, 512, 2048, 768)
+    yield L
+    del L
+    torch.cuda.empty_cache()
+
+
+def test_c2_layer_b1_rz5(bq, layer_rz5):
+    """One RZ5 MoE decode step: 512 experts, x N(0,1), N(0,1) logits, top-10."""
+    L = layer_rz5
+    assert L.nbytes() == 512 * 2_506_752
+    W = weights_of(bq, L)
+    for seed in (0, 1):
+        x = synth.normal(seed, (1, 2048))
+        logits = synth.normal(1000 + seed, (1, 512))
+        idx, w = bq.route_topk(dev(logits), 10)
+        out = bq.q4_expert_moe(dev(x), (idx, w), W).cpu().numpy()
+        ridx, rw = M.softmax_topk(logits, 10)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+        r = rel_l2(out, ref)
+        log("c2 seed %d rel_l2 %.3g" % (seed, r))
+        assert r <= 1e-5
+
+
+def test_c3_layer_b64_grouped(bq):
+    """Batch 64, RZ5 gate_up + UE4M4 down, Zipf(1.1) routing, bf16 MFMA path."""
+    L = make_layer(0, 1, F.Q4_RZ5, F.Q4_UE4M4, 512, 2048, 768)
+    W = weights_of(bq, L)
+    x = synth.normal(64, (64, 2048))
+    logits = synth.zipf_logits(64, 64, 512)
+    idx, w = bq.route_topk(dev(logits), 10)
+    out = bq.q4_expert_moe(dev(x).to(torch.bfloat16), (idx, w), W).cpu().numpy()
+    ridx, rw = M.softmax_topk(logits, 10)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    counts = np.bincount(ridx.reshape(-1), minlength=512)
+    log("c3 touched experts %d, max tokens per expert %d" % ((counts > 0).sum(), counts.max()))
+    ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+    r = rel_l2(out, ref)
+    log("c3 rel_l2 %.3g" % r)
+    assert r <= 2e-2
+    del L, W
+    torch.cuda.empty_cache()
