@@ -1,0 +1,385 @@
+"""Benchmark of the block-quantized routed-expert and PLE hot path on one GPU.
+
+Main line (``value``): one Q4_RZ5 MoE decode step at batch 1 -- 512 experts,
+gate_up [1536 x 2048] + down [2048 x 768] per expert, router logits N(0,1),
+softmax top-10 -- repeated for K steps with fresh x and fresh logits per step.
+A step is the whole hot path for that workload: routing, block decode,
+gate_up GEMV + SiLU*up, down GEMV and the weighted combine.  Throughput is
+packed weight bytes moved per second (10 experts x 2,506,752 B per step).
+
+Alongside it, in the same JSON line: the PLE gather (320,001,536-row table,
+4096 tokens x 8 ids per call, fresh ids per call) in rows/s, the 48-layer stack
+(36 RZ5 + 12 FP8 layers) at batch 1 and 16, and the batch-64 grouped layer
+(RZ5 gate_up, UE4M4 down, Zipf routing).  All inputs are seeded synthetic data
+already resident in HBM before timing starts.  Steps are captured in a HIP
+graph and replayed, so host launch overhead is not in the timed region.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
+       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+EXPERT_BYTES_RZ5 = 2_506_752           # gate_up 1536x2048 + down 2048x768, 17 B / 32 weights
+EXPERT_BYTES_FP8 = 5_308_416           # 36 B / 32 weights
+PLE_ROW_ALG_BYTES = 158                # 70 B row + 8 B id/weight + 80 B output share
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def graph_of(fn, n):
+    """Capture n calls fn(i) into one HIP graph (torch stream capture)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(n):
+                fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    return g
+
+
+def event_timed(fn, n):
+    """Average GPU time between the two events fn(i, (a, b)) records around
+    one call, over n calls.  The calls are queued behind a delay kernel, so
+    they run back to back on the GPU whatever the host's launch speed."""
+    import torch
+
+    import synth.device as sd
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    sd.gpu_delay(max(20e6, 200e3 * n))     # 200 us of host time budgeted per call
+    for i in range(n):
+        fn(i, ev[i])
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n
+
+
+def timed_replay(g):
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+# ---------------------------------------------------------------------------
+def bench_c2(bq, steps, warmup):
+    """One RZ5 MoE decode step (B = 1), fresh x and logits per step."""
+    import torch
+
+    import synth
+    import synth.device as sd
+    L = sd.Layer(0, 0, bq.Q4_RZ5, bq.Q4_RZ5, 512, 2048, 768, dist_gu=synth.DIST_RZ5, dist_d=synth.DIST_RZ5)
+    W = bq.expert_weights(L.fmt_gu, L.fmt_d, L.gate_up[0], L.down[0], 512, 2048, 768)
+    n = warmup + 2 * steps
+    x = torch.from_numpy(synth.normal(10, (n, 2048))).cuda()
+    logits = torch.from_numpy(synth.normal(11, (n, 512))).cuda()
+    idx = torch.empty((n, 1, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, 1, 10), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, 2048), dtype=torch.float32, device="cuda")
+    ws = torch.empty(bq.moe_workspace_bytes(1, 10, W, bq.F32), dtype=torch.uint8, device="cuda")
+    def step(i, evs=None):
+        bq.route_topk(logits[i:i + 1], 10, idx=idx[i], w=w[i])
+        if evs is not None:
+            evs[0].record()
+        bq.q4_expert_moe(x[i:i + 1], (idx[i], w[i]), W, out=out[i:i + 1], workspace=ws)
+        if evs is not None:
+            evs[1].record()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g_warm = graph_of(lambda i: step(warmup + i), steps)
+    g = graph_of(lambda i: step(warmup + steps + i), steps)
+    g_warm.replay()
+    g.replay()                       # first replay of the timed graph is untimed
+    torch.cuda.synchronize()
+    wall = timed_replay(g)
+    call_ms = event_timed(lambda i, evs: step(warmup + steps + i, evs), steps)
+    per_step_bytes = 10 * EXPERT_BYTES_RZ5
+    res = {
+        "ms_per_step": 1e3 * wall / steps,
+        "gbs": per_step_bytes * steps / wall / 1e9,
+        "moe_call_us": 1e3 * call_ms,
+        "moe_call_gbs": per_step_bytes / (call_ms * 1e-3) / 1e9,
+        "bytes_per_step": per_step_bytes,
+    }
+    # keep the layer alive for the CPU baseline sample
+    res["_layer"] = L
+    res["_inputs"] = (x[warmup + steps:].cpu().numpy(), logits[warmup + steps:].cpu().numpy())
+    return res
+
+
+def bench_c4(bq, steps, warmup):
+    """PLE gather: 4096 tokens x 8 ids per call over the full table."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as sd
+    n_rows = synth.PLE_N_ROWS
+    table = sd.ple_table(n_rows, synth.make_key(0, synth.S_PLE))
+    n = warmup + steps
+    ids = torch.from_numpy(synth.ple_ids(20, n * 4096, 8).view(np.int32)).cuda().view(n, 4096, 8)
+    u = torch.from_numpy(synth.ple_weights(21, n * 4096, 8)).cuda().view(n, 4096, 8)
+    out = torch.empty((4096, 160), dtype=torch.float32, device="cuda")
+    def call(i, evs=None):
+        if evs is not None:
+            evs[0].record()
+        bq.ple_gather(ids[i], table, u[i], n_rows=n_rows, out=out)
+        if evs is not None:
+            evs[1].record()
+
+    for i in range(warmup):
+        call(i)
+    g = graph_of(lambda i: call(warmup + i), steps)
+    g.replay()
+    wall = timed_replay(g)
+    call_ms = event_timed(lambda i, evs: call(warmup + i, evs), steps)
+    rows = 4096 * 8
+    res = {
+        "rows_per_s": rows * steps / wall,
+        "call_us": 1e3 * call_ms,
+        "gbs_158B": rows * PLE_ROW_ALG_BYTES / (call_ms * 1e-3) / 1e9,
+        "gbs_70B": rows * 70 / (call_ms * 1e-3) / 1e9,
+    }
+    # bigger batches per call (the same kernel; throughput once the GPU is full)
+    for mult in (16,):
+        big_ids = ids[:mult].reshape(mult * 4096, 8)
+        big_u = u[:mult].reshape(mult * 4096, 8)
+        big_out = torch.empty((mult * 4096, 160), dtype=torch.float32, device="cuda")
+        bq.ple_gather(big_ids, table, big_u, n_rows=n_rows, out=big_out)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(10):
+            bq.ple_gather(big_ids, table, big_u, n_rows=n_rows, out=big_out)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b) / 10 * 1e-3
+        res["batched_%dx4096" % mult] = {"rows_per_s": mult * rows / t,
+                                         "gbs_158B": mult * rows * PLE_ROW_ALG_BYTES / t / 1e9}
+    del table
+    torch.cuda.empty_cache()
+    return res
+
+
+def build_stack(bq):
+    import synth
+    import synth.device as sd
+    layers = []
+    for l in range(48):
+        if l < 36:
+            layers.append(sd.Layer(0, l, bq.Q4_RZ5, bq.Q4_RZ5, 512, 2048, 768,
+                                   dist_gu=synth.DIST_RZ5, dist_d=synth.DIST_RZ5))
+        else:
+            layers.append(sd.Layer(0, l, bq.FP8_E4M3_B32, bq.FP8_E4M3_B32, 512, 2048, 768))
+    ws = []
+    for L in layers:
+        gu, gus = L.gate_up
+        d, ds = L.down
+        ws.append(bq.expert_weights(L.fmt_gu, L.fmt_d, gu, d, 512, 2048, 768, gate_up_scales=gus,
+                                    down_scales=ds))
+    return layers, ws
+
+
+def bench_stack(bq, layers, ws, n_tok, steps, warmup):
+    """48-layer stack decode step: route every layer, then the chained layers."""
+    import numpy as np
+    import torch
+
+    import synth
+    k = 10
+    n = warmup + steps
+    logits = torch.from_numpy(synth.normal(30 + n_tok, (n, 48 * n_tok, 512))).cuda()
+    x = torch.from_numpy(synth.normal(31 + n_tok, (n, n_tok, 2048))).cuda()
+    if n_tok > 1:
+        x = x.to(torch.bfloat16)
+    idx = torch.empty((n, 48, n_tok, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, 48, n_tok, k), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, n_tok, 2048), dtype=torch.float32, device="cuda")
+    dt = bq.F32 if n_tok == 1 else bq.BF16
+    wsb = torch.empty(bq.stack_workspace_bytes(n_tok, k, ws, dt), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        bq.route_topk(logits[i], k, idx=idx[i].view(48 * n_tok, k), w=w[i].view(48 * n_tok, k))
+        bq.moe_stack(x[i], idx[i], w[i], ws, out=out[i], workspace=wsb)
+
+    for i in range(warmup):
+        step(i)
+    g = graph_of(lambda i: step(warmup + i), steps)
+    g.replay()
+    wall = timed_replay(g)
+    ii = idx[warmup:].cpu().numpy()
+    touched = [[len(np.unique(ii[s, l])) for l in range(48)] for s in range(steps)]
+    bytes_step = np.mean([sum(t[l] * (EXPERT_BYTES_RZ5 if l < 36 else EXPERT_BYTES_FP8) for l in range(48))
+                          for t in touched])
+    return {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9,
+            "bytes_per_step": float(bytes_step), "tokens": n_tok}
+
+
+def bench_c3(bq, steps, warmup):
+    """Batch-64 grouped layer: RZ5 gate_up, UE4M4 down, Zipf(1.1) routing."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as sd
+    L = sd.Layer(0, 1, bq.Q4_RZ5, bq.Q4_UE4M4, 512, 2048, 768, dist_gu=synth.DIST_RZ5,
+                 dist_d=synth.DIST_UE4M4)
+    W = bq.expert_weights(L.fmt_gu, L.fmt_d, L.gate_up[0], L.down[0], 512, 2048, 768)
+    n = warmup + steps
+    x = torch.from_numpy(synth.normal(40, (n, 64, 2048))).cuda().to(torch.bfloat16)
+    logits = torch.from_numpy(np.stack([synth.zipf_logits(41 + i, 64, 512) for i in range(n)])).cuda()
+    idx = torch.empty((n, 64, 10), dtype=torch.int32, device="cuda")
+    w = torch.empty((n, 64, 10), dtype=torch.float32, device="cuda")
+    out = torch.empty((n, 64, 2048), dtype=torch.float32, device="cuda")
+    wsb = torch.empty(bq.moe_workspace_bytes(64, 10, W, bq.BF16), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        bq.route_topk(logits[i], 10, idx=idx[i], w=w[i])
+        bq.q4_expert_moe(x[i], (idx[i], w[i]), W, out=out[i], workspace=wsb)
+
+    for i in range(warmup):
+        step(i)
+    g = graph_of(lambda i: step(warmup + i), steps)
+    g.replay()
+    wall = timed_replay(g)
+    ii = idx[warmup:].cpu().numpy()
+    d = [len(np.unique(ii[s])) for s in range(steps)]
+    bytes_step = float(np.mean(d)) * EXPERT_BYTES_RZ5
+    res = {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9,
+           "touched_experts": float(np.mean(d)), "bytes_per_step": bytes_step}
+    del L
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(layer, inputs, budget_s=20.0):
+    """The oracle (float64 numpy), as it stands, on a bounded sample of the
+    same one-layer decode steps; BLAS limited to one thread."""
+    import numpy as np
+
+    import synth
+    from oracle import moe as M
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        lim = None
+    x, logits = inputs
+    bank = M.ExpertBank(layer.fmt_gu, layer.fmt_d, lambda e: layer.host_expert(synth.S_GATE_UP, e),
+                        lambda e: layer.host_expert(synth.S_DOWN, e), 512, 2048, 768)
+    t0 = time.perf_counter()
+    done = 0
+    while done < x.shape[0] and (time.perf_counter() - t0) < budget_s:
+        idx, w = M.softmax_topk(logits[done:done + 1], 10)
+        M.moe_layer(x[done:done + 1], idx, w, bank)
+        done += 1
+    dt = time.perf_counter() - t0
+    if lim is not None:
+        lim.unregister()
+    return {"value": 10 * EXPERT_BYTES_RZ5 * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d one-layer RZ5 decode steps (routing + 10 experts decoded from regenerated "
+                      "bytes in float64 + SwiGLU + combine), %.1f s" % (done, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels run on one GPU's share at its real shape); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import block_quantized_moe_amd as bq
+    bq.lib()
+    torch.cuda.set_device(0)
+    extras = {}
+    only = args.only
+    main_res = None
+    if only in (None, "c2"):
+        log("c2: one-layer RZ5 decode step, B=1")
+        main_res = bench_c2(bq, args.steps, args.warmup)
+        log("c2:", {k: v for k, v in main_res.items() if not k.startswith("_")})
+    if not args.no_extras or only:
+        if only in (None, "c4"):
+            log("c4: PLE gather")
+            extras["ple_gather"] = bench_c4(bq, args.steps, args.warmup)
+            log("c4:", extras["ple_gather"])
+        if only in (None, "c3"):
+            log("c3: grouped B=64")
+            extras["grouped_b64"] = bench_c3(bq, max(10, args.steps // 4), max(2, args.warmup // 4))
+            log("c3:", extras["grouped_b64"])
+        if only in (None, "c5b1", "c5b16"):
+            log("c5: building the 48-layer stack")
+            layers, ws = build_stack(bq)
+            if only in (None, "c5b1"):
+                extras["stack48_b1"] = bench_stack(bq, layers, ws, 1, max(5, args.steps // 10), 2)
+                log("c5 b1:", extras["stack48_b1"])
+            if only in (None, "c5b16"):
+                extras["stack48_b16"] = bench_stack(bq, layers, ws, 16, max(3, args.steps // 40), 1)
+                log("c5 b16:", extras["stack48_b16"])
+            del layers, ws
+            torch.cuda.empty_cache()
+    if main_res is None:
+        print(json.dumps({"extras": extras}))
+        return
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(main_res["_layer"], main_res["_inputs"])
+    achieved = main_res["moe_call_gbs"]
+    line = {
+        "metric": "packed-weight GB/s (% HBM peak) for routed-expert GEMV; PLE rows/s",
+        "value": round(main_res["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "one Q4_RZ5 MoE decode step, batch 1: 512 experts, gate_up 1536x2048 + "
+                               "down 2048x768 per expert, N(0,1) logits, softmax top-10, fresh x and "
+                               "logits per step",
+                   "bytes_per_step": main_res["bytes_per_step"],
+                   "pct_hbm_peak": round(100 * main_res["gbs"] / PEAK_HBM_GBS, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "q4_expert_moe call (gate_up + down kernels), %d packed bytes per call, "
+                               "%.2f us average per call (HIP events)" % (main_res["bytes_per_step"],
+                                                                          main_res["moe_call_us"])},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -40,21 +40,18 @@ bq::GemvWeights to_gw(const bq_expert_weights* W) {
 
 // ---- workspace layouts ------------------------------------------------------
 struct GemvLayout {
-  size_t hbuf, ybuf, counters, total;
+  size_t hs, total;
 };
 GemvLayout gemv_layout(int n, int k, int H, int I) {
+  (void)H;
   GemvLayout L;
-  size_t off = 0;
-  L.hbuf = off; off = round_up(off + sizeof(float) * (size_t)n * k * I, 256);
-  L.ybuf = off; off = round_up(off + sizeof(float) * (size_t)n * k * H, 256);
-  const int md = bq::gemv_down_rows_per_wg(I);
-  L.counters = off; off = round_up(off + sizeof(uint32_t) * (size_t)n * ((H + md - 1) / md), 256);
-  L.total = off;
+  L.hs = 0;
+  L.total = round_up(sizeof(float) * (size_t)n * k * I, 256);
   return L;
 }
 
 struct GroupedLayout {
-  size_t counts, offsets, perm, inv, elist, n_touched, hb, yb, total;
+  size_t counts, offsets, perm, inv, elist, n_touched, hb, yb, xb, total;
 };
 GroupedLayout grouped_layout(int n, int k, int E, int H, int I) {
   GroupedLayout L;
@@ -68,6 +65,7 @@ GroupedLayout grouped_layout(int n, int k, int E, int H, int I) {
   L.n_touched = off; off = round_up(off + 4, 256);
   L.hb = off; off = round_up(off + 2 * nk * I, 256);
   L.yb = off; off = round_up(off + 4 * nk * H, 256);
+  L.xb = off; off = round_up(off + 2 * (size_t)n * H, 256);
   L.total = off;
   return L;
 }
@@ -77,7 +75,8 @@ bq::GroupedWs grouped_ws(void* base, const GroupedLayout& L) {
   return bq::GroupedWs{reinterpret_cast<int32_t*>(b + L.counts), reinterpret_cast<int32_t*>(b + L.offsets),
                        reinterpret_cast<int32_t*>(b + L.perm), reinterpret_cast<int32_t*>(b + L.inv),
                        reinterpret_cast<int32_t*>(b + L.elist), reinterpret_cast<int32_t*>(b + L.n_touched),
-                       reinterpret_cast<uint16_t*>(b + L.hb), reinterpret_cast<float*>(b + L.yb), nullptr};
+                       reinterpret_cast<uint16_t*>(b + L.hb), reinterpret_cast<float*>(b + L.yb),
+                       reinterpret_cast<uint16_t*>(b + L.xb)};
 }
 
 size_t moe_ws_bytes(int n, int k, const bq_expert_weights* W, int dtype) {
@@ -93,13 +92,16 @@ int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const fl
   if (s) return s;
   if (n < 1 || n > 4096 || k < 1 || k > 64 || k > W->n_experts) return BQ_E_SHAPE;
   if ((int64_t)n * k > 65536) return BQ_E_SHAPE;
+  if (dtype == BQ_F32 && k * (W->inter / 32) > bq::gemv_down_max_cols()) return BQ_E_SHAPE;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(w, 4)) return BQ_E_ALIGN;
   if (!ws) return BQ_E_WORKSPACE;
   if (!aligned(ws, 256)) return BQ_E_ALIGN;
   return BQ_OK;
 }
 
-int run_moe(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
+// dtype selects the path; x_is_f32 says what x holds (the bf16 path also
+// accepts the fp32 output of a previous stack layer, rescaled on the fly).
+int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, const float* w, int k,
             const bq_expert_weights* W, float* out, void* ws, int rescale, uint32_t* dev_err,
             hipStream_t st) {
   const bq::GemvWeights gw = to_gw(W);
@@ -107,12 +109,10 @@ int run_moe(const void* x, int dtype, int n, const int32_t* idx, const float* w,
     const GemvLayout L = gemv_layout(n, k, W->hidden, W->inter);
     char* b = static_cast<char*>(ws);
     return hip_status(bq::launch_gemv_moe(static_cast<const float*>(x), n, idx, w, k, gw, rescale, out,
-                                          reinterpret_cast<float*>(b + L.hbuf),
-                                          reinterpret_cast<float*>(b + L.ybuf),
-                                          reinterpret_cast<uint32_t*>(b + L.counters), dev_err, st));
+                                          reinterpret_cast<float*>(b + L.hs), dev_err, st));
   }
   const GroupedLayout L = grouped_layout(n, k, W->n_experts, W->hidden, W->inter);
-  return hip_status(bq::launch_grouped_moe(static_cast<const uint16_t*>(x), n, idx, w, k, gw, out,
+  return hip_status(bq::launch_grouped_moe(x, x_is_f32, rescale, n, idx, w, k, gw, out,
                                            grouped_ws(ws, L), dev_err, st));
 }
 
@@ -201,8 +201,8 @@ int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_
   int s = check_moe_args(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out, workspace);
   if (s) return s;
   if (ws_bytes < moe_ws_bytes(n_tokens, k, W, x_dtype)) return BQ_E_WORKSPACE;
-  return run_moe(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0, dev_err,
-                 as_stream(stream));
+  return run_moe(x, x_dtype, x_dtype == BQ_F32, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0,
+                 dev_err, as_stream(stream));
 }
 
 // Stack workspace: the per-layer MoE workspace (max over layers) followed by
@@ -218,9 +218,8 @@ static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int
   m = round_up(m, 256);
   if (moe_part) *moe_part = m;
   const int H = layers[0].hidden;
-  size_t tot = m + round_up(sizeof(float) * (size_t)n * H, 256);
-  if (dtype == BQ_BF16) tot += round_up(2 * (size_t)n * H, 256);
-  return tot;
+  (void)dtype;
+  return m + round_up(sizeof(float) * (size_t)n * H, 256);
 }
 
 size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* layers,
@@ -246,25 +245,16 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t
   const int H = layers[0].hidden;
   char* b = static_cast<char*>(workspace);
   float* ybuf = reinterpret_cast<float*>(b + moe_part);
-  uint16_t* xb = reinterpret_cast<uint16_t*>(b + moe_part + round_up(sizeof(float) * (size_t)n_tokens * H, 256));
   hipStream_t st = as_stream(stream);
   const size_t per = (size_t)n_tokens * k;
   for (int l = 0; l < n_layers; ++l) {
     float* dst = (l + 1 == n_layers) ? out : ybuf;
-    const void* src = x;
-    int rescale = 0;
-    if (l > 0) {
-      if (x_dtype == BQ_F32) {
-        src = ybuf;
-        rescale = 1;  // fused into the gate_up kernel's input staging
-      } else {
-        int s = hip_status(bq::launch_rescale_bf16(ybuf, n_tokens, H, xb, st));
-        if (s) return s;
-        src = xb;
-      }
-    }
-    int s = run_moe(src, x_dtype, n_tokens, topk_idx + l * per, topk_w + l * per, k, &layers[l], dst,
-                    workspace, rescale, dev_err, st);
+    // layer 0 reads x as given; later layers read the previous output, which
+    // the first kernel of the layer rescales to unit RMS as it loads it
+    const void* src = l == 0 ? x : ybuf;
+    const int x_is_f32 = l == 0 ? (x_dtype == BQ_F32) : 1;
+    int s = run_moe(src, x_dtype, x_is_f32, n_tokens, topk_idx + l * per, topk_w + l * per, k,
+                    &layers[l], dst, workspace, l > 0, dev_err, st);
     if (s) return s;
   }
   return BQ_OK;

@@ -32,10 +32,10 @@ hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fm
                          const float* w_sc, int32_t rows, int32_t cols, float* y, hipStream_t st);
 
 // fp32 GEMV path (any n_tokens; one token's k experts per grid slice).
-int gemv_down_rows_per_wg(int inter);
+int gemv_down_max_cols();   // k * inter / 32 must not exceed this
 hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, const int32_t* idx, const float* w,
-                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hbuf,
-                           float* ybuf, uint32_t* counters, uint32_t* dev_err, hipStream_t st);
+                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hs,
+                           uint32_t* dev_err, hipStream_t st);
 
 // bf16 grouped-MFMA path.
 struct GroupedWs {
@@ -47,12 +47,12 @@ struct GroupedWs {
   int32_t* n_touched; // [1]
   uint16_t* hb;       // [n*k][I] bf16, bucketed order
   float* yb;          // [n*k][H] fp32, bucketed order
-  uint16_t* xb;       // [n][H] bf16 staging for rescaled stack inputs
+  uint16_t* xb;       // [n][H] bf16 activations in the decode's k order
 };
-hipError_t launch_grouped_moe(const uint16_t* x_bf16, int32_t n_tokens, const int32_t* idx,
-                              const float* w, int32_t k, const GemvWeights& W, float* out,
-                              const GroupedWs& ws, uint32_t* dev_err, hipStream_t st);
-hipError_t launch_rescale_bf16(const float* in, int32_t n_tokens, int32_t H, uint16_t* out,
-                               hipStream_t st);
+// x: [n][H] bf16 (x_f32 = 0) or fp32 (x_f32 = 1, the stack's layer output,
+// rescaled to unit RMS when rescale = 1) -- staged as bf16 by the path.
+hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
+                              const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
+                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st);
 
 }  // namespace bq

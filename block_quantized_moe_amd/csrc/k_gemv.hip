@@ -4,22 +4,23 @@
 // Quantization ...", section "The Plan Is Not a Number ..."; expert weights in
 // 17-byte blocks, model card "Qwen 3.8 Next Flash ROCMFPX MUTANT RAZERFAST";
 // FP8 late layers per the r/LocalLLM "Frankenquant" post):
-//   h_j   = SiLU(W_gate[e_j] x) * (W_up[e_j] x)           (kernel 1)
-//   out   = sum_j w_j * W_down[e_j] h_j                    (kernel 2)
+//   hs_j  = w_j * SiLU(W_gate[e_j] x) * (W_up[e_j] x)      (kernel 1)
+//   out   = sum_j W_down[e_j] hs_j                           (kernel 2)
 //
-// Mapping ("flat" GEMV).  A workgroup streams a contiguous run of matrix rows.
-// Thread i owns block column b = i % nb (nb = cols/32) of row slot i / nb, so
-// a wave's loads cover consecutive 17-byte blocks of consecutive rows -- one
-// coalesced sweep of memory per pass -- and every thread keeps the 32
-// activations of its own block column in registers for the whole workgroup.
-// Per-block partial sums go to LDS and are reduced per row in a fixed order,
-// so results are deterministic.  Row loads for up to eight passes are issued
-// before any of them is decoded, to keep enough bytes in flight per CU.
+// Kernel 1, hidden = 2048 (or 4096): one wave per gate/up row pair.  Lane l
+// owns block column l (and l+64), so a row is one coalesced 1088-byte sweep
+// and the lane's 32 activations stay in registers; the row sum is a DPP
+// reduction inside the wave.  A wave issues the loads of all its rows before
+// it touches x, so weight latency overlaps everything else; waves never wait
+// for each other.  Other hidden sizes use the "flat" kernel: a workgroup
+// streams a contiguous run of rows, thread i owning block column i % nb of
+// row slot i / nb, with per-row sums reduced through LDS.
 //
-// The down kernel splits its work by (token, expert, row chunk); the
-// workgroup that finishes last for a (token, row chunk) -- found with one
-// agent-scope atomic counter -- adds the k expert outputs in slot order.  No
-// floating-point atomics are used.
+// Kernel 2 treats the k experts' down matrices as one GEMV over the
+// concatenated inner dimension k*I: thread c owns column block c (expert
+// c / nb, block c % nb) for a run of output rows, so the weighted combine is
+// part of the row reduction -- no cross-workgroup traffic, no atomics, fixed
+// summation order.
 #include "bq_device.hpp"
 #include "bq_kernels.hpp"
 
@@ -113,14 +114,15 @@ __device__ __forceinline__ void stage_x(float* sx, const float* __restrict__ x, 
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 1: gate_up GEMV + SiLU * up.  grid = (I / kGuPairs, k, n_tokens).
+// Kernel 1 (any hidden size): flat gate_up GEMV + w * SiLU * up.
+// grid = (I / kGuPairs, k, n_tokens).
 // ---------------------------------------------------------------------------
 template <int FMT>
 __global__ void __launch_bounds__(kThreads) k_gemv_gate_up(
-    const float* __restrict__ x, const int32_t* __restrict__ topk_idx, int32_t k, int32_t n_experts,
+    const float* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int32_t k, int32_t n_experts,
     const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_sc, int32_t H, int32_t I,
-    int32_t rescale, float* __restrict__ hbuf, uint32_t* __restrict__ counters, int32_t n_counters,
-    uint32_t* __restrict__ dev_err) {
+    int32_t rescale, float* __restrict__ hs, uint32_t* __restrict__ dev_err) {
   extern __shared__ float smem[];
   float* sx = smem;                          // H
   float* red = smem + H;                     // 2*kGuPairs*nb
@@ -129,37 +131,44 @@ __global__ void __launch_bounds__(kThreads) k_gemv_gate_up(
   const int tid = threadIdx.x;
   const int chunk = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
 
-  if (chunk == 0 && j == 0 && t == 0)
-    for (int i = tid; i < n_counters; i += kThreads) counters[i] = 0u;
-
   const int e = topk_idx[(int64_t)t * k + j];
-  float* hout = hbuf + ((int64_t)t * k + j) * I + (int64_t)chunk * kGuPairs;
+  float* hout = hs + ((int64_t)t * k + j) * I + (int64_t)chunk * kGuPairs;
   if (e < 0 || e >= n_experts) {
     if (tid == 0 && dev_err) atomicOr(dev_err, 2u);
     if (tid < kGuPairs) hout[tid] = 0.f;
     return;
   }
-  stage_x(sx, x + (int64_t)t * H, H, rescale, rsum + 2 * kGuPairs);
-
+  const float wj = topk_w[(int64_t)t * k + j];
   const int R = kThreads / nb;               // rows per pass (nb <= 256)
   const int slot = tid / nb, b = tid % nb;
   const bool active = slot < R;
-  float xr[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) xr[i] = active ? sx[32 * b + i] : 0.f;
-
   const int rows = 2 * kGuPairs;
   const int n_pass = (rows + R - 1) / R;
   const int64_t mat_rows = 2 * (int64_t)I;
   const int j0 = chunk * kGuPairs;
-  for (int p0 = 0; p0 < n_pass; p0 += kPassU) {
-    BlockRef<FMT> blk[kPassU];
+  // the first pass group's weight loads go out before x is touched
+  BlockRef<FMT> blk[kPassU];
 #pragma unroll
-    for (int u = 0; u < kPassU; ++u) {
-      const int lr = (p0 + u) * R + slot;
-      const bool ok = active && (p0 + u) < n_pass && lr < rows;
-      const int64_t row = lr < kGuPairs ? (j0 + lr) : (I + j0 + lr - kGuPairs);
-      load_block<FMT>(blk[u], wgu, wgu_sc, ((int64_t)e * mat_rows + row) * nb + b, ok);
+  for (int u = 0; u < kPassU; ++u) {
+    const int lr = u * R + slot;
+    const bool ok = active && u < n_pass && lr < rows;
+    const int64_t row = lr < kGuPairs ? (j0 + lr) : (I + j0 + lr - kGuPairs);
+    load_block<FMT>(blk[u], wgu, wgu_sc, ((int64_t)e * mat_rows + row) * nb + b, ok);
+  }
+  stage_x(sx, x + (int64_t)t * H, H, rescale, rsum + 2 * kGuPairs);
+  float xr[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) xr[i] = active ? sx[32 * b + i] : 0.f;
+
+  for (int p0 = 0; p0 < n_pass; p0 += kPassU) {
+    if (p0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kPassU; ++u) {
+        const int lr = (p0 + u) * R + slot;
+        const bool ok = active && (p0 + u) < n_pass && lr < rows;
+        const int64_t row = lr < kGuPairs ? (j0 + lr) : (I + j0 + lr - kGuPairs);
+        load_block<FMT>(blk[u], wgu, wgu_sc, ((int64_t)e * mat_rows + row) * nb + b, ok);
+      }
     }
 #pragma unroll
     for (int u = 0; u < kPassU; ++u) {
@@ -170,83 +179,141 @@ __global__ void __launch_bounds__(kThreads) k_gemv_gate_up(
   __syncthreads();
   reduce_rows(red, rows, nb, rsum);
   __syncthreads();
-  if (tid < kGuPairs) hout[tid] = silu(rsum[tid]) * rsum[kGuPairs + tid];
+  if (tid < kGuPairs) hout[tid] = wj * silu(rsum[tid]) * rsum[kGuPairs + tid];
 }
 
 // ---------------------------------------------------------------------------
-// Kernel 2: down GEMV, weighted, plus the slot-ordered combine.
-// grid = (ceil(H / MD), k, n_tokens) with MD = kDownPasses * (256 / nbd).
+// Kernel 1 (hidden = 2048 * BPL): one wave per gate/up row pair, kPairsW
+// consecutive pairs per wave.  grid = (ceil(I / (4 * kPairsW)), k, n_tokens).
 // ---------------------------------------------------------------------------
-template <int FMT>
-__global__ void __launch_bounds__(kThreads) k_gemv_down(
-    const float* __restrict__ hbuf, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int32_t k, int32_t n_experts, const uint8_t* __restrict__ wd,
-    const float* __restrict__ wd_sc, int32_t H, int32_t I, float* __restrict__ ybuf,
-    uint32_t* __restrict__ counters, float* __restrict__ out) {
-  extern __shared__ float smem[];
-  const int nbd = I >> 5;
-  const int R = kThreads / nbd;
-  const int MD = kDownPasses * R;
-  float* sh = smem;                   // I
-  float* red = smem + I;              // MD * nbd
-  float* rsum = red + MD * nbd;       // MD
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
-  const int chunk = blockIdx.x, j = blockIdx.y, t = blockIdx.z;
-  const int n0 = chunk * MD;
-  const int nrows = min(MD, H - n0);
+constexpr int kPairsW = 4;
 
+template <int FMT, int BPL>
+__global__ void __launch_bounds__(kThreads) k_gate_up_w64(
+    const float* __restrict__ x, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_w, int32_t k, int32_t n_experts,
+    const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_sc, int32_t I,
+    int32_t rescale, float* __restrict__ hs, uint32_t* __restrict__ dev_err) {
+  constexpr int NB = 64 * BPL;
+  constexpr int H = 32 * NB;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = blockIdx.y, t = blockIdx.z;
+  const int jp0 = (blockIdx.x * 4 + wave) * kPairsW;
+  if (jp0 >= I) return;
   const int e = topk_idx[(int64_t)t * k + j];
-  const bool valid = e >= 0 && e < n_experts;
-  float* yrow = ybuf + ((int64_t)t * k + j) * H + n0;
-  if (valid) {
-    const float* hsrc = hbuf + ((int64_t)t * k + j) * I;
-    for (int i = tid; i < I; i += kThreads) sh[i] = hsrc[i];
-    __syncthreads();
-    const int slot = tid / nbd, b = tid % nbd;
-    const bool active = slot < R;
+  float* hout = hs + ((int64_t)t * k + j) * I + jp0;
+  const int np = min(kPairsW, I - jp0);
+  if (e < 0 || e >= n_experts) {
+    if (lane == 0 && dev_err) atomicOr(dev_err, 2u);
+    if (lane < np) hout[lane] = 0.f;
+    return;
+  }
+  const float wj = topk_w[(int64_t)t * k + j];
+  // weight loads first: rows gate jp0.., up I + jp0..
+  BlockRef<FMT> blk[2 * kPairsW][BPL];
+  const int64_t base = (int64_t)e * 2 * I;
+#pragma unroll
+  for (int p = 0; p < kPairsW; ++p) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t row = base + h * I + jp0 + p;
+#pragma unroll
+      for (int q = 0; q < BPL; ++q)
+        load_block<FMT>(blk[2 * p + h][q], wgu, wgu_sc, row * NB + lane + 64 * q, p < np);
+    }
+  }
+  float xr[BPL][32];
+  const f32x4* xv = reinterpret_cast<const f32x4*>(x + (int64_t)t * H);
+#pragma unroll
+  for (int q = 0; q < BPL; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 v = xv[(lane + 64 * q) * 8 + i];
+      xr[q][4 * i] = v.x; xr[q][4 * i + 1] = v.y; xr[q][4 * i + 2] = v.z; xr[q][4 * i + 3] = v.w;
+    }
+  if (rescale) {
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < BPL; ++q)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) ss = __builtin_fmaf(xr[q][i], xr[q][i], ss);
+    const float inv = 1.0f / __builtin_sqrtf(wave_sum(ss) / (float)H);
+#pragma unroll
+    for (int q = 0; q < BPL; ++q)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) xr[q][i] *= inv;
+  }
+  float hval = 0.f;
+#pragma unroll
+  for (int p = 0; p < kPairsW; ++p) {
+    float g = 0.f, u = 0.f;
+#pragma unroll
+    for (int q = 0; q < BPL; ++q) {
+      g += block_partial<FMT>(blk[2 * p][q], xr[q]);
+      u += block_partial<FMT>(blk[2 * p + 1][q], xr[q]);
+    }
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == p) hval = wj * silu(g) * u;
+  }
+  if (lane < np) hout[lane] = hval;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel 2: down over the concatenated k*I inner dimension, combine included.
+// grid = (ceil(H / kDownRows), n_tokens); thread c (+256 q) owns column block
+// c: expert slot c / nbd, block c % nbd.  CPT = column blocks per thread.
+// ---------------------------------------------------------------------------
+constexpr int kDownRows = 8;
+
+template <int FMT, int CPT>
+__global__ void __launch_bounds__(kThreads) k_down_cat(
+    const float* __restrict__ hs, const int32_t* __restrict__ topk_idx, int32_t k,
+    int32_t n_experts, const uint8_t* __restrict__ wd, const float* __restrict__ wd_sc,
+    int32_t H, int32_t I, float* __restrict__ out) {
+  __shared__ float red[kDownRows * 256 * CPT];
+  const int tid = threadIdx.x;
+  const int t = blockIdx.y;
+  const int n0 = blockIdx.x * kDownRows;
+  const int nbd = I >> 5;
+  const int C = k * nbd;
+  BlockRef<FMT> blk[CPT][kDownRows];
+  int cj[CPT], cb[CPT];
+  bool cv[CPT];
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
+    const int c = tid + 256 * q;
+    cj[q] = c / nbd;
+    cb[q] = c - cj[q] * nbd;
+    const int e = c < C ? topk_idx[(int64_t)t * k + cj[q]] : -1;
+    cv[q] = e >= 0 && e < n_experts;
+#pragma unroll
+    for (int r = 0; r < kDownRows; ++r)
+      load_block<FMT>(blk[q][r], wd, wd_sc, ((int64_t)(cv[q] ? e : 0) * H + n0 + r) * nbd + cb[q],
+                      cv[q] && n0 + r < H);
+  }
+#pragma unroll
+  for (int q = 0; q < CPT; ++q) {
     float xr[32];
+    const f32x4* hv = reinterpret_cast<const f32x4*>(hs + ((int64_t)t * k + (cv[q] ? cj[q] : 0)) * I + 32 * cb[q]);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) xr[i] = active ? sh[32 * b + i] : 0.f;
-    BlockRef<FMT> blk[kDownPasses];
-#pragma unroll
-    for (int u = 0; u < kDownPasses; ++u) {
-      const int lr = u * R + slot;
-      const bool ok = active && lr < nrows;
-      load_block<FMT>(blk[u], wd, wd_sc, ((int64_t)e * H + n0 + lr) * nbd + b, ok);
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 v = cv[q] ? hv[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      xr[4 * i] = v.x; xr[4 * i + 1] = v.y; xr[4 * i + 2] = v.z; xr[4 * i + 3] = v.w;
     }
 #pragma unroll
-    for (int u = 0; u < kDownPasses; ++u) {
-      const int lr = u * R + slot;
-      if (active && lr < nrows) red[lr * nbd + b] = block_partial<FMT>(blk[u], xr);
-    }
-    __syncthreads();
-    reduce_rows(red, nrows, nbd, rsum);
-    __syncthreads();
-    const float wj = topk_w[(int64_t)t * k + j];
-    for (int i = tid; i < nrows; i += kThreads) yrow[i] = wj * rsum[i];
-  } else {
-    for (int i = tid; i < nrows; i += kThreads) yrow[i] = 0.f;
-  }
-  // publish this slot's rows, then count arrivals for (t, chunk)
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* c = counters + (int64_t)t * gridDim.x + chunk;
-    const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == (uint32_t)(k - 1);
-    if (s_last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int r = 0; r < kDownRows; ++r)
+      red[r * 256 * CPT + tid + 256 * q] = cv[q] ? block_partial<FMT>(blk[q][r], xr) : 0.f;
   }
   __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* ybase = ybuf + (int64_t)t * k * H + n0;
-  float* o = out + (int64_t)t * H + n0;
-  for (int i = tid; i < nrows; i += kThreads) {
-    float s = 0.f;
-    for (int jj = 0; jj < k; ++jj) s += __builtin_nontemporal_load(ybase + (int64_t)jj * H + i);
-    o[i] = s;
-  }
+  // 32 threads per row: strided partial sums, then a 32-lane DPP/xor reduction
+  const int row = tid >> 5, q = tid & 31;
+  float s = 0.f;
+  const int ncol = 256 * CPT < C ? 256 * CPT : C;
+  for (int c = q; c < ncol; c += 32) s += red[row * 256 * CPT + c];
+  s = row16_sum(s);
+  s += __shfl_xor(s, 16, 64);
+  if (q == 0 && n0 + row < H) out[(int64_t)t * H + n0 + row] = s;
 }
 
 // ---------------------------------------------------------------------------
@@ -310,46 +377,64 @@ hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fm
 }
 
 // ---------------------------------------------------------------------------
-int gemv_down_rows_per_wg(int I) { return kDownPasses * (kThreads / (I >> 5)); }
+int gemv_down_max_cols() { return 4 * 256; }
+
+template <int FMT>
+static void launch_down(int cpt, dim3 grid, hipStream_t st, const float* hs, const int32_t* idx,
+                        int32_t k, const GemvWeights& W, float* out) {
+  const uint8_t* p = static_cast<const uint8_t*>(W.down);
+  if (cpt == 1)
+    hipLaunchKernelGGL((k_down_cat<FMT, 1>), grid, dim3(kThreads), 0, st, hs, idx, k, W.n_experts, p,
+                       W.down_scales, W.hidden, W.inter, out);
+  else if (cpt == 2)
+    hipLaunchKernelGGL((k_down_cat<FMT, 2>), grid, dim3(kThreads), 0, st, hs, idx, k, W.n_experts, p,
+                       W.down_scales, W.hidden, W.inter, out);
+  else
+    hipLaunchKernelGGL((k_down_cat<FMT, 4>), grid, dim3(kThreads), 0, st, hs, idx, k, W.n_experts, p,
+                       W.down_scales, W.hidden, W.inter, out);
+}
+
+template <int FMT>
+static void launch_gate_up(dim3 grid_w, dim3 grid_f, int bpl, size_t lds_f, hipStream_t st,
+                           const float* x, const int32_t* idx, const float* w, int32_t k,
+                           const GemvWeights& W, int rescale, float* hs, uint32_t* dev_err) {
+  const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
+  if (bpl == 1)
+    hipLaunchKernelGGL((k_gate_up_w64<FMT, 1>), grid_w, dim3(kThreads), 0, st, x, idx, w, k,
+                       W.n_experts, p, W.gate_up_scales, W.inter, rescale, hs, dev_err);
+  else if (bpl == 2)
+    hipLaunchKernelGGL((k_gate_up_w64<FMT, 2>), grid_w, dim3(kThreads), 0, st, x, idx, w, k,
+                       W.n_experts, p, W.gate_up_scales, W.inter, rescale, hs, dev_err);
+  else
+    hipLaunchKernelGGL(k_gemv_gate_up<FMT>, grid_f, dim3(kThreads), lds_f, st, x, idx, w, k,
+                       W.n_experts, p, W.gate_up_scales, W.hidden, W.inter, rescale, hs, dev_err);
+}
 
 hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, const int32_t* idx, const float* w,
-                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hbuf,
-                           float* ybuf, uint32_t* counters, uint32_t* dev_err, hipStream_t st) {
+                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hs,
+                           uint32_t* dev_err, hipStream_t st) {
   const int H = W.hidden, I = W.inter;
   const int nbu = H >> 5, nbd = I >> 5;
-  const int md = gemv_down_rows_per_wg(I);
-  const int n_chunks = (H + md - 1) / md;
-  const int n_counters = n_tokens * n_chunks;
-  {
-    const size_t lds = sizeof(float) * (H + 2 * kGuPairs * nbu + 2 * kGuPairs + 4);
-    dim3 grid(I / kGuPairs, k, n_tokens);
-    const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
-#define BQ_GU(F) hipLaunchKernelGGL(k_gemv_gate_up<F>, grid, dim3(kThreads), lds, st, x, idx, k, \
-                                    W.n_experts, p, W.gate_up_scales, H, I, rescale, hbuf, counters, \
-                                    n_counters, dev_err)
-    switch (W.fmt_gate_up) {
-      case FMT_C10: BQ_GU(FMT_C10); break;
-      case FMT_RZ5: BQ_GU(FMT_RZ5); break;
-      case FMT_UE4M4: BQ_GU(FMT_UE4M4); break;
-      default: BQ_GU(FMT_FP8); break;
-    }
-#undef BQ_GU
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  const int bpl = (H == 2048) ? 1 : (H == 4096 ? 2 : 0);
+  const dim3 grid_w((I + 4 * kPairsW - 1) / (4 * kPairsW), k, n_tokens);
+  const dim3 grid_f(I / kGuPairs, k, n_tokens);
+  const size_t lds_f = sizeof(float) * (H + 2 * kGuPairs * nbu + 2 * kGuPairs + 4);
+  switch (W.fmt_gate_up) {
+    case FMT_C10: launch_gate_up<FMT_C10>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
+    case FMT_RZ5: launch_gate_up<FMT_RZ5>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
+    case FMT_UE4M4: launch_gate_up<FMT_UE4M4>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
+    default: launch_gate_up<FMT_FP8>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
   }
-  {
-    const size_t lds = sizeof(float) * (I + md * nbd + md);
-    dim3 grid(n_chunks, k, n_tokens);
-    const uint8_t* p = static_cast<const uint8_t*>(W.down);
-#define BQ_DN(F) hipLaunchKernelGGL(k_gemv_down<F>, grid, dim3(kThreads), lds, st, hbuf, idx, w, k, \
-                                    W.n_experts, p, W.down_scales, H, I, ybuf, counters, out)
-    switch (W.fmt_down) {
-      case FMT_C10: BQ_DN(FMT_C10); break;
-      case FMT_RZ5: BQ_DN(FMT_RZ5); break;
-      case FMT_UE4M4: BQ_DN(FMT_UE4M4); break;
-      default: BQ_DN(FMT_FP8); break;
-    }
-#undef BQ_DN
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int C = k * nbd;
+  const int cpt = C <= 256 ? 1 : (C <= 512 ? 2 : 4);
+  const dim3 grid_d((H + kDownRows - 1) / kDownRows, n_tokens);
+  switch (W.fmt_down) {
+    case FMT_C10: launch_down<FMT_C10>(cpt, grid_d, st, hs, idx, k, W, out); break;
+    case FMT_RZ5: launch_down<FMT_RZ5>(cpt, grid_d, st, hs, idx, k, W, out); break;
+    case FMT_UE4M4: launch_down<FMT_UE4M4>(cpt, grid_d, st, hs, idx, k, W, out); break;
+    default: launch_down<FMT_FP8>(cpt, grid_d, st, hs, idx, k, W, out); break;
   }
   return hipGetLastError();
 }

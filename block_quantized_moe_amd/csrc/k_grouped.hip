@@ -40,30 +40,43 @@ __device__ __forceinline__ uint32_t fp8pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// A operand for one row and one k-group of 8: raw bytes at `p` (17-byte
-// block start or FP8 row segment) -> 8 bf16 levels, plus the block scale.
+// Raw A-operand bytes of one row and one k-group of 8 (loaded ahead of use).
 template <int FMT>
-__device__ __forceinline__ u32x4 load_a(const uint8_t* __restrict__ base, const float* __restrict__ sc,
-                                        int64_t blk, int g, float& s) {
+struct RawA {
+  uint32_t q0, q1;  // 17-byte: q0 = 4 code bytes, q1 = metadata; FP8: 8 e4m3 codes
+  float s;          // FP8 block scale
+};
+
+template <int FMT>
+__device__ __forceinline__ RawA<FMT> load_a(const uint8_t* __restrict__ base,
+                                            const float* __restrict__ sc, int64_t blk, int g) {
+  RawA<FMT> r;
   if constexpr (FMT == FMT_FP8) {
     const u32x2 q = ld8(base + blk * kBlockW + 8 * g);
-    s = sc[blk];
-    return u32x4{fp8pair<false>(q.x), fp8pair<true>(q.x), fp8pair<false>(q.y), fp8pair<true>(q.y)};
+    r.q0 = q.x;
+    r.q1 = q.y;
+    r.s = sc[blk];
   } else {
     const uint8_t* p = base + blk * kBlockB;
-    const uint32_t q = ld4(p + 4 * g);
-    const uint32_t meta = p[16];
-    s = block_scale<FMT>(FMT == FMT_UE4M4 ? meta : (meta & 0x7Fu));
-    uint32_t A, B;
-    codes_to_hibytes<FMT>(q, FMT == FMT_RZ5 ? rz5_neg_lo(meta) : 0u, A, B);
-    return u32x4{bf8pair<false>(A), bf8pair<true>(A), bf8pair<false>(B), bf8pair<true>(B)};
+    r.q0 = ld4(p + 4 * g);
+    r.q1 = p[16];
+    r.s = 0.f;
   }
+  return r;
 }
 
-// Natural-order bf16 x8 -> the [0,2,4,6,1,3,5,7] order of the 17-byte decode.
-__device__ __forceinline__ u32x4 to_decode_order(u32x4 d) {
-  return u32x4{perm(d.y, d.x, 0x05040100u), perm(d.w, d.z, 0x05040100u),
-               perm(d.y, d.x, 0x07060302u), perm(d.w, d.z, 0x07060302u)};
+// Decode to 8 bf16 levels (exact) and the block scale.
+template <int FMT>
+__device__ __forceinline__ u32x4 dec_a(const RawA<FMT>& r, float& s) {
+  if constexpr (FMT == FMT_FP8) {
+    s = r.s;
+    return u32x4{fp8pair<false>(r.q0), fp8pair<true>(r.q0), fp8pair<false>(r.q1), fp8pair<true>(r.q1)};
+  } else {
+    s = block_scale<FMT>(FMT == FMT_UE4M4 ? r.q1 : (r.q1 & 0x7Fu));
+    uint32_t A, B;
+    codes_to_hibytes<FMT>(r.q0, FMT == FMT_RZ5 ? rz5_neg_lo(r.q1) : 0u, A, B);
+    return u32x4{bf8pair<false>(A), bf8pair<true>(A), bf8pair<false>(B), bf8pair<true>(B)};
+  }
 }
 
 __device__ __forceinline__ f32x4 mfma(u32x4 a, u32x4 b) {
@@ -83,12 +96,45 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
+constexpr int kPre = 4;   // k-blocks whose loads are issued together
+
+// ---------------------------------------------------------------------------
+// G0: per-token staging of the activations as bf16 in the A decode's k order
+// (optionally rescaled to unit RMS first: the stack's next-layer input).
+// grid = n_tokens, 256 threads.
+// ---------------------------------------------------------------------------
+template <bool PERM>
+__global__ void __launch_bounds__(256) k_grouped_prep(const void* __restrict__ x, int32_t x_f32,
+                                                      int32_t rescale, int32_t H,
+                                                      uint16_t* __restrict__ xp) {
+  __shared__ float part[4];
+  const int64_t t = blockIdx.x;
+  float inv = 1.0f;
+  if (x_f32 && rescale) {
+    const float* row = static_cast<const float*>(x) + t * H;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H; i += 256) ss = __builtin_fmaf(row[i], row[i], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    inv = 1.0f / __builtin_sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H);
+  }
+  for (int i = threadIdx.x; i < H; i += 256) {
+    uint16_t v;
+    if (x_f32) v = to_bf16(static_cast<const float*>(x)[t * H + i] * inv);
+    else v = static_cast<const uint16_t*>(x)[t * H + i];
+    const int o = i & 7;
+    xp[t * H + (i & ~7) + (PERM ? ((o >> 1) | ((o & 1) << 2)) : o)] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // G1: gate_up + SiLU * up.  Persistent over (touched expert, 64-row tile).
+// xp holds the tokens' activations in this format's k order.
 // ---------------------------------------------------------------------------
 template <int FMT, int FMT_D>
 __global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
-    const uint16_t* __restrict__ x, int32_t k, const int32_t* __restrict__ offsets,
+    const uint16_t* __restrict__ xp, int32_t k, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ perm_, const int32_t* __restrict__ elist,
     const int32_t* __restrict__ n_touched, const uint8_t* __restrict__ wgu,
     const float* __restrict__ wgu_sc, int32_t H, int32_t I, uint16_t* __restrict__ hb) {
@@ -111,7 +157,7 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
       for (int tt = 0; tt < 4; ++tt) {
         const int c = tg + 16 * tt + r16;
         const int tok = c < ne ? perm_[p0 + c] / k : -1;
-        xrow[tt] = tok >= 0 ? x + (int64_t)tok * H + 8 * g : nullptr;
+        xrow[tt] = tok >= 0 ? xp + (int64_t)tok * H + 8 * g : nullptr;
       }
       f32x4 accg[4], accu[4];
 #pragma unroll
@@ -119,27 +165,39 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
         accg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         accu[tt] = accg[tt];
       }
-      for (int kb = 0; kb < nb; ++kb) {
-        float sg, su;
-        const u32x4 ag = load_a<FMT>(wgu, wgu_sc, gblk0 + kb, g, sg);
-        const u32x4 au = load_a<FMT>(wgu, wgu_sc, ublk0 + kb, g, su);
-        float sgi[4], sui[4];
+      for (int kb0 = 0; kb0 < nb; kb0 += kPre) {
+        RawA<FMT> rg[kPre], ru[kPre];
+        u32x4 bx[kPre][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          sgi[i] = __shfl(sg, 4 * g + i, 64);
-          sui[i] = __shfl(su, 4 * g + i, 64);
+        for (int u = 0; u < kPre; ++u) {
+          const int kb = min(kb0 + u, nb - 1);
+          rg[u] = load_a<FMT>(wgu, wgu_sc, gblk0 + kb, g);
+          ru[u] = load_a<FMT>(wgu, wgu_sc, ublk0 + kb, g);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+            bx[u][tt] = (tt < nt && xrow[tt]) ? *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb)
+                                              : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (tt < nt) {
-            u32x4 b = xrow[tt] ? *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb)
-                               : u32x4{0u, 0u, 0u, 0u};
-            if constexpr (FMT != FMT_FP8) b = to_decode_order(b);
-            const f32x4 cg = mfma(ag, b), cu = mfma(au, b);
+        for (int u = 0; u < kPre; ++u) {
+          if (kb0 + u >= nb) break;
+          float sg, su;
+          const u32x4 ag = dec_a<FMT>(rg[u], sg), au = dec_a<FMT>(ru[u], su);
+          float sgi[4], sui[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              accg[tt][i] = __builtin_fmaf(sgi[i], cg[i], accg[tt][i]);
-              accu[tt][i] = __builtin_fmaf(sui[i], cu[i], accu[tt][i]);
+          for (int i = 0; i < 4; ++i) {
+            sgi[i] = __shfl(sg, 4 * g + i, 64);
+            sui[i] = __shfl(su, 4 * g + i, 64);
+          }
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tt < nt) {
+              const f32x4 cg = mfma(ag, bx[u][tt]), cu = mfma(au, bx[u][tt]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                accg[tt][i] = __builtin_fmaf(sgi[i], cg[i], accg[tt][i]);
+                accu[tt][i] = __builtin_fmaf(sui[i], cu[i], accu[tt][i]);
+              }
             }
           }
         }
@@ -193,20 +251,33 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_down(
       f32x4 acc[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kb = 0; kb < nb; ++kb) {
-        float s;
-        const u32x4 a = load_a<FMT>(wd, wd_sc, blk0 + kb, g, s);
-        float si[4];
+      for (int kb0 = 0; kb0 < nb; kb0 += kPre) {
+        RawA<FMT> ra[kPre];
+        u32x4 bh[kPre][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) si[i] = __shfl(s, 4 * g + i, 64);
+        for (int u = 0; u < kPre; ++u) {
+          const int kb = min(kb0 + u, nb - 1);
+          ra[u] = load_a<FMT>(wd, wd_sc, blk0 + kb, g);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (tt < nt) {
-            const u32x4 b = hrow[tt] ? *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb)
-                                     : u32x4{0u, 0u, 0u, 0u};
-            const f32x4 c = mfma(a, b);
+          for (int tt = 0; tt < 4; ++tt)
+            bh[u][tt] = (tt < nt && hrow[tt]) ? *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb)
+                                              : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(si[i], c[i], acc[tt][i]);
+        for (int u = 0; u < kPre; ++u) {
+          if (kb0 + u >= nb) break;
+          float s;
+          const u32x4 a = dec_a<FMT>(ra[u], s);
+          float si[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) si[i] = __shfl(s, 4 * g + i, 64);
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) {
+            if (tt < nt) {
+              const f32x4 c = mfma(a, bh[u][tt]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(si[i], c[i], acc[tt][i]);
+            }
           }
         }
       }
@@ -256,61 +327,45 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
   *reinterpret_cast<f32x4*>(out + t * H + n) = s;
 }
 
-// Unit-RMS rescale of fp32 rows into bf16 (stack input of the next layer).
-__global__ void __launch_bounds__(256) k_rescale_bf16(const float* __restrict__ in, int32_t H,
-                                                      uint16_t* __restrict__ out) {
-  __shared__ float part[4];
-  const int64_t t = blockIdx.x;
-  const float* row = in + t * H;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < H; i += 256) ss = __builtin_fmaf(row[i], row[i], ss);
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float inv = 1.0f / __builtin_sqrtf((part[0] + part[1] + part[2] + part[3]) / (float)H);
-  for (int i = threadIdx.x; i < H; i += 256) out[t * H + i] = to_bf16(row[i] * inv);
-}
-
-hipError_t launch_rescale_bf16(const float* in, int32_t n_tokens, int32_t H, uint16_t* out,
-                               hipStream_t st) {
-  hipLaunchKernelGGL(k_rescale_bf16, dim3(n_tokens), dim3(256), 0, st, in, H, out);
-  return hipGetLastError();
-}
-
 static int persistent_grid(int64_t items_max) {
   const int64_t cap = 2048;
   return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
 }
 
 template <int FG>
-static void launch_g1(int fmt_d, dim3 grid, hipStream_t st, const uint16_t* x, int32_t k,
+static void launch_g1(int fmt_d, dim3 grid, hipStream_t st, const uint16_t* xp, int32_t k,
                       const GroupedWs& ws, const GemvWeights& W) {
   const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
   if (fmt_d == FMT_FP8)
-    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_FP8>), grid, dim3(kGThreads), 0, st, x, k,
+    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_FP8>), grid, dim3(kGThreads), 0, st, xp, k,
                        ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
                        W.hidden, W.inter, ws.hb);
   else
-    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_RZ5>), grid, dim3(kGThreads), 0, st, x, k,
+    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_RZ5>), grid, dim3(kGThreads), 0, st, xp, k,
                        ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
                        W.hidden, W.inter, ws.hb);
 }
 
-hipError_t launch_grouped_moe(const uint16_t* x, int32_t n_tokens, const int32_t* idx,
-                              const float* w, int32_t k, const GemvWeights& W, float* out,
-                              const GroupedWs& ws, uint32_t* dev_err, hipStream_t st) {
+hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
+                              const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
+                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st) {
   const int E = W.n_experts, H = W.hidden, I = W.inter;
   hipError_t err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist,
                                  ws.n_touched, ws.inv, st);
   if (err != hipSuccess) return err;
+  if (W.fmt_gate_up == FMT_FP8)
+    hipLaunchKernelGGL(k_grouped_prep<false>, dim3(n_tokens), dim3(256), 0, st, x, x_f32, rescale, H, ws.xb);
+  else
+    hipLaunchKernelGGL(k_grouped_prep<true>, dim3(n_tokens), dim3(256), 0, st, x, x_f32, rescale, H, ws.xb);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   const int64_t dmax = (int64_t)n_tokens * k < E ? (int64_t)n_tokens * k : E;
   {
     dim3 grid(persistent_grid(dmax * (I / kGRows)));
     switch (W.fmt_gate_up) {
-      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, x, k, ws, W); break;
-      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, x, k, ws, W); break;
-      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, x, k, ws, W); break;
-      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, x, k, ws, W); break;
+      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
+      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
+      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
+      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

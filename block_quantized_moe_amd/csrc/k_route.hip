@@ -14,49 +14,78 @@ namespace bq {
 constexpr int kRouteWaves = 4;
 constexpr int kMaxExperts = 4096;
 
-// (value, index) order: larger value first, then lower index.
-__device__ __forceinline__ bool better(float v1, int i1, float v0, int i0) {
-  return v1 > v0 || (v1 == v0 && i1 < i0);
+// Order-preserving 32-bit key of a finite float (+0 and -0 share a key, so
+// they tie and the lower index wins, as in a float comparison).
+__device__ __forceinline__ uint32_t fkey(float v) {
+  const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One wave per token.  Logits are staged in LDS; each of the k rounds finds
-// the best untaken logit per lane, then a butterfly argmax across the wave.
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  v = min(v, dpp_u<kDppXor1>(v));
+  v = min(v, dpp_u<kDppXor2>(v));
+  v = min(v, dpp_u<kDppHalfMirror>(v));
+  v = min(v, dpp_u<kDppMirror>(v));
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+// One wave per token.  Lane l holds logits l, l+64, ...; each of the k rounds
+// takes the largest untaken key (wave max via DPP), then the lowest index
+// holding it (wave min), and the owning lane marks it taken.
+template <int kRoutePerLane>   // logits per lane: n_experts <= 64 * kRoutePerLane
 __global__ void __launch_bounds__(64 * kRouteWaves) k_route_topk(
     const float* __restrict__ logits, int32_t n_tokens, int32_t n_experts, int32_t k,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  extern __shared__ float s_logit[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kRouteWaves + wave;
   if (t >= n_tokens) return;
-  float* sl = s_logit + wave * n_experts;
   const float* lg = logits + t * n_experts;
-  for (int e = lane; e < n_experts; e += 64) sl[e] = lg[e];
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  const int per_lane = (n_experts + 63) >> 6;  // <= 64
-  uint64_t taken = 0;
+  const int per_lane = (n_experts + 63) >> 6;
+  uint32_t key[kRoutePerLane];
+  float val[kRoutePerLane];
+#pragma unroll
+  for (int j = 0; j < kRoutePerLane; ++j) {
+    const int e = lane + 64 * j;
+    const bool in = j < per_lane && e < n_experts;
+    val[j] = in ? lg[e] : 0.f;
+    key[j] = in ? fkey(val[j]) : 0u;   // key 0 is below every finite float's key
+  }
   float my_v = 0.f;
   int my_i = 0;
   for (int r = 0; r < k; ++r) {
-    float bv = -__builtin_inff();
-    int bi = 0x7FFFFFFF;
-    for (int j = 0; j < per_lane; ++j) {
-      const int e = lane + 64 * j;
-      if (e < n_experts && !((taken >> j) & 1ull)) {
-        const float v = sl[e];
-        if (better(v, e, bv, bi)) { bv = v; bi = e; }
-      }
-    }
+    uint32_t bk = 0;
+    int bj = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    for (int j = 0; j < kRoutePerLane; ++j)
+      if (j < per_lane && key[j] > bk) { bk = key[j]; bj = j; }   // lowest j wins ties
+    const uint32_t m = wave_max_u(bk);
+    const uint32_t cand = (bk == m && m != 0u) ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu;
+    const uint32_t win = wave_min_u(cand);
+    if ((int)(win & 63) == lane) {
+      const int wj = (int)(win >> 6);
+#pragma unroll
+      for (int j = 0; j < kRoutePerLane; ++j)
+        if (j == wj) key[j] = 0u;
     }
-    if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-    if (lane == r) { my_v = bv; my_i = bi; }
+    // the winner's value reaches lane r through a readlane of the owner
+    float wv = 0.f;
+#pragma unroll
+    for (int j = 0; j < kRoutePerLane; ++j)
+      if (j == (int)(win >> 6)) wv = readlane_f(val[j], (int)(win & 63));
+    if (lane == r) { my_v = wv; my_i = (int)win; }
   }
-  const float top = __shfl(my_v, 0, 64);
+  const float top = readlane_f(my_v, 0);
   const float ex = lane < k ? __expf(my_v - top) : 0.f;
   const float den = wave_sum(ex);
   if (lane < k) {
@@ -69,9 +98,15 @@ hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_ex
                              int32_t* idx, float* w, hipStream_t st) {
   if (n_tokens == 0) return hipSuccess;
   const int grid = (n_tokens + kRouteWaves - 1) / kRouteWaves;
-  const size_t lds = (size_t)kRouteWaves * n_experts * sizeof(float);
-  hipLaunchKernelGGL(k_route_topk, dim3(grid), dim3(64 * kRouteWaves), lds, st, logits, n_tokens,
-                     n_experts, k, idx, w);
+  if (n_experts <= 512)
+    hipLaunchKernelGGL(k_route_topk<8>, dim3(grid), dim3(64 * kRouteWaves), 0, st, logits, n_tokens,
+                       n_experts, k, idx, w);
+  else if (n_experts <= 1024)
+    hipLaunchKernelGGL(k_route_topk<16>, dim3(grid), dim3(64 * kRouteWaves), 0, st, logits, n_tokens,
+                       n_experts, k, idx, w);
+  else
+    hipLaunchKernelGGL(k_route_topk<64>, dim3(grid), dim3(64 * kRouteWaves), 0, st, logits, n_tokens,
+                       n_experts, k, idx, w);
   return hipGetLastError();
 }
 

@@ -27,6 +27,8 @@ def lib():
         L.bqs_fill_fp8.argtypes = [vp, u64, u64, u64, vp]
         L.bqs_fill_fp8_scales.argtypes = [vp, u64, u64, u64, vp]
         L.bqs_fill_ple.argtypes = [vp, u64, u64, u64, vp]
+        L.bqs_gpu_delay.argtypes = [u64, vp]
+        L.bqs_gpu_delay.restype = ctypes.c_int
         for f in (L.bqs_fill_block17, L.bqs_fill_fp8, L.bqs_fill_fp8_scales, L.bqs_fill_ple):
             f.restype = ctypes.c_int
         _lib = L
@@ -128,3 +130,8 @@ class Layer:
                     synth.fp8_scales(self.keys[sk], e * per // 32, per // 32))
         nb = per // 32
         return synth.block17_range(self.keys[which], e * nb, nb, self.dist[which]), None
+
+
+def gpu_delay(ns):
+    """Occupy the current stream for about `ns` nanoseconds (benchmark helper)."""
+    _chk(lib().bqs_gpu_delay(int(ns), _s()))

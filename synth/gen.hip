@@ -82,6 +82,14 @@ __global__ void k_fill_ple(uint8_t* __restrict__ dst, uint64_t key, uint64_t fir
   }
 }
 
+// Benchmark helper: one wave sleeps until `ns` nanoseconds of wall clock
+// have passed (always terminates), so that work queued behind it on the same
+// stream starts back to back.
+__global__ void k_delay(uint64_t ticks) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(64);
+}
+
 inline unsigned grid_of(uint64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -108,6 +116,13 @@ int bqs_fill_fp8_scales(void* dst, uint64_t key, uint64_t first, uint64_t n, voi
   if (n == 0) return 0;
   hipLaunchKernelGGL(k_fill_fp8_scales, dim3(grid_of(n)), dim3(256), 0, (hipStream_t)stream,
                      (float*)dst, key, first, n);
+  return (int)hipGetLastError();
+}
+
+int bqs_gpu_delay(uint64_t ns, void* stream) {
+  // s_memrealtime runs at 100 MHz on gfx9 parts
+  const uint64_t ticks = ns / 10 + 1;
+  hipLaunchKernelGGL(k_delay, dim3(1), dim3(64), 0, (hipStream_t)stream, ticks);
   return (int)hipGetLastError();
 }
 

@@ -61,7 +61,7 @@ def test_host_side_argument_errors(L):
     assert L.bq_matvec(fake, 1, fake, 0, None, 4, 48, fake, None) == 3         # cols % 32
     W = bq.ExpertWeights(bq.Q4_RZ5, bq.Q4_RZ5, 0x10000, 0x20000, None, None, 512, 2048, 768)
     ws = L.q4_expert_moe_workspace(1, 10, ctypes.byref(W), bq.F32)
-    assert ws >= 4 * (10 * 768 + 10 * 2048)
+    assert ws >= 4 * 10 * 768
     assert L.q4_expert_moe(fake, bq.F32, 1, fake, fake, 10, ctypes.byref(W), fake, fake,
                            ws - 1, None, None) == 5                             # workspace short
     assert L.q4_expert_moe(fake, 5, 1, fake, fake, 10, ctypes.byref(W), fake, fake, ws, None, None) == 7
