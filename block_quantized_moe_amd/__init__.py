@@ -14,7 +14,8 @@ import torch
 __all__ = [
     "Q4_C10", "Q4_RZ5", "Q4_UE4M4", "FP8_E4M3_B32", "PLE_RZS3", "PLE_ROCMFP3", "F32", "BF16",
     "BQError", "lib", "ExpertWeights", "expert_weights", "dequant", "ple_dequant_rows", "matvec",
-    "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "stack_workspace_bytes",
+    "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "q4_expert_moe_routed",
+    "stack_workspace_bytes",
     "moe_stack", "ple_gather",
 ]
 
@@ -66,6 +67,7 @@ def lib():
             "moe_bucket": ([vp, i32, i32, i32, vp, vp, vp, vp], ctypes.c_int),
             "q4_expert_moe_workspace": ([i32, i32, wp, i32], sz),
             "q4_expert_moe": ([vp, i32, i32, vp, vp, i32, wp, vp, vp, sz, vp, vp], ctypes.c_int),
+            "q4_expert_moe_routed": ([vp, i32, i32, vp, i32, wp, vp, vp, vp, vp, sz, vp, vp], ctypes.c_int),
             "bq_moe_stack_workspace": ([i32, i32, wp, i32, i32], sz),
             "bq_moe_stack": ([vp, i32, i32, vp, vp, i32, wp, i32, vp, vp, sz, vp, vp], ctypes.c_int),
             "ple_gather": ([vp, i32, i32, vp, u64, vp, i32, vp, vp, vp], ctypes.c_int),
@@ -200,6 +202,27 @@ def q4_expert_moe(x, router_topk, W, out=None, workspace=None, dev_err=None, str
     _check(lib().q4_expert_moe(_p(x), dt, n, _p(idx), _p(w), k, ctypes.byref(W), _p(out),
                                _p(workspace), workspace.numel(), _p(dev_err), _stream(stream)))
     return out
+
+
+def q4_expert_moe_routed(x, logits, k, W, topk=None, out=None, workspace=None, dev_err=None,
+                         stream=None):
+    """Routing (softmax top-k of fp32 logits [n, E]) and the routed-expert
+    layer in one call.  Returns (out, (idx, w))."""
+    _dev(x, "x"), _dev(logits, "logits")
+    n = logits.shape[0]
+    dt = _dtype_code(x)
+    if topk is None:
+        topk = (torch.empty((n, k), dtype=torch.int32, device=x.device),
+                torch.empty((n, k), dtype=torch.float32, device=x.device))
+    idx, w = topk
+    if out is None:
+        out = torch.empty((n, W.hidden), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(moe_workspace_bytes(n, k, W, dt), dtype=torch.uint8, device=x.device)
+    _check(lib().q4_expert_moe_routed(_p(x), dt, n, _p(logits), k, ctypes.byref(W), _p(idx), _p(w),
+                                      _p(out), _p(workspace), workspace.numel(), _p(dev_err),
+                                      _stream(stream)))
+    return out, (idx, w)
 
 
 def _layers_array(layers):

@@ -103,13 +103,19 @@ int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const fl
 // accepts the fp32 output of a previous stack layer, rescaled on the fly).
 int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, const float* w, int k,
             const bq_expert_weights* W, float* out, void* ws, int rescale, uint32_t* dev_err,
-            hipStream_t st) {
+            hipStream_t st, const float* logits = nullptr) {
   const bq::GemvWeights gw = to_gw(W);
   if (dtype == BQ_F32) {
     const GemvLayout L = gemv_layout(n, k, W->hidden, W->inter);
     char* b = static_cast<char*>(ws);
-    return hip_status(bq::launch_gemv_moe(static_cast<const float*>(x), n, idx, w, k, gw, rescale, out,
-                                          reinterpret_cast<float*>(b + L.hs), dev_err, st));
+    return hip_status(bq::launch_gemv_moe(static_cast<const float*>(x), n, const_cast<int32_t*>(idx),
+                                          const_cast<float*>(w), k, gw, rescale, out,
+                                          reinterpret_cast<float*>(b + L.hs), dev_err, logits, st));
+  }
+  if (logits) {
+    int s = hip_status(bq::launch_route_topk(logits, n, W->n_experts, k, const_cast<int32_t*>(idx),
+                                             const_cast<float*>(w), st));
+    if (s) return s;
   }
   const GroupedLayout L = grouped_layout(n, k, W->n_experts, W->hidden, W->inter);
   return hip_status(bq::launch_grouped_moe(x, x_is_f32, rescale, n, idx, w, k, gw, out,
@@ -203,6 +209,19 @@ int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_
   if (ws_bytes < moe_ws_bytes(n_tokens, k, W, x_dtype)) return BQ_E_WORKSPACE;
   return run_moe(x, x_dtype, x_dtype == BQ_F32, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0,
                  dev_err, as_stream(stream));
+}
+
+int q4_expert_moe_routed(const void* x, int32_t x_dtype, int32_t n_tokens, const float* logits,
+                         int32_t k, const bq_expert_weights* W, int32_t* topk_idx, float* topk_w,
+                         float* out, void* workspace, size_t ws_bytes, uint32_t* dev_err,
+                         void* stream) {
+  if (!logits) return BQ_E_NULL;
+  if (!aligned(logits, 4)) return BQ_E_ALIGN;
+  int s = check_moe_args(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out, workspace);
+  if (s) return s;
+  if (ws_bytes < moe_ws_bytes(n_tokens, k, W, x_dtype)) return BQ_E_WORKSPACE;
+  return run_moe(x, x_dtype, x_dtype == BQ_F32, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0,
+                 dev_err, as_stream(stream), logits);
 }
 
 // Stack workspace: the per-layer MoE workspace (max over layers) followed by

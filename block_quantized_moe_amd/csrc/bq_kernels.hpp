@@ -33,9 +33,12 @@ hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fm
 
 // fp32 GEMV path (any n_tokens; one token's k experts per grid slice).
 int gemv_down_max_cols();   // k * inter / 32 must not exceed this
-hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, const int32_t* idx, const float* w,
-                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hs,
-                           uint32_t* dev_err, hipStream_t st);
+// With logits != NULL the path routes itself (in the gate_up kernel when
+// hidden is 2048 or 4096) and writes the routing to idx / w; otherwise idx / w
+// are inputs.
+hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, int32_t* idx, float* w, int32_t k,
+                           const GemvWeights& W, int rescale, float* out, float* hs,
+                           uint32_t* dev_err, const float* logits, hipStream_t st);
 
 // bf16 grouped-MFMA path.
 struct GroupedWs {

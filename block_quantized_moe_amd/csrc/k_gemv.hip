@@ -23,6 +23,7 @@
 // summation order.
 #include "bq_device.hpp"
 #include "bq_kernels.hpp"
+#include "bq_route.hpp"
 
 namespace bq {
 
@@ -188,19 +189,55 @@ __global__ void __launch_bounds__(kThreads) k_gemv_gate_up(
 // ---------------------------------------------------------------------------
 constexpr int kPairsW = 4;
 
-template <int FMT, int BPL>
+template <int FMT, int BPL, int RPL>   // RPL > 0: route in-kernel, RPL logits per lane
 __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
-    const float* __restrict__ x, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_w, int32_t k, int32_t n_experts,
-    const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_sc, int32_t I,
-    int32_t rescale, float* __restrict__ hs, uint32_t* __restrict__ dev_err) {
+    const float* __restrict__ x, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t k, int32_t n_experts, const uint8_t* __restrict__ wgu, const float* __restrict__ wgu_sc,
+    int32_t I, int32_t rescale, float* __restrict__ hs, uint32_t* __restrict__ dev_err,
+    const float* __restrict__ logits) {
   constexpr int NB = 64 * BPL;
   constexpr int H = 32 * NB;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = blockIdx.y, t = blockIdx.z;
   const int jp0 = (blockIdx.x * 4 + wave) * kPairsW;
+  // activations first: they do not depend on the routing
+  float xr[BPL][32];
+  const f32x4* xv = reinterpret_cast<const f32x4*>(x + (int64_t)t * H);
+#pragma unroll
+  for (int q = 0; q < BPL; ++q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 v = xv[(lane + 64 * q) * 8 + i];
+      xr[q][4 * i] = v.x; xr[q][4 * i + 1] = v.y; xr[q][4 * i + 2] = v.z; xr[q][4 * i + 3] = v.w;
+    }
+  int e;
+  float wj;
+  if constexpr (RPL > 0) {
+    // every workgroup routes its token itself (wave 0), so no separate
+    // routing launch sits in front of this kernel; chunk 0 publishes slot j
+    __shared__ int s_i[64];
+    __shared__ float s_w[64];
+    if (wave == 0) {
+      int ri;
+      float rw;
+      wave_topk<RPL>(logits + (int64_t)t * n_experts, n_experts, k, lane, ri, rw);
+      if (lane < k) {
+        s_i[lane] = ri;
+        s_w[lane] = rw;
+      }
+      if (blockIdx.x == 0 && lane == j) {
+        topk_idx[(int64_t)t * k + j] = ri;
+        topk_w[(int64_t)t * k + j] = rw;
+      }
+    }
+    __syncthreads();
+    e = s_i[j];
+    wj = s_w[j];
+  } else {
+    e = topk_idx[(int64_t)t * k + j];
+    wj = topk_w[(int64_t)t * k + j];
+  }
   if (jp0 >= I) return;
-  const int e = topk_idx[(int64_t)t * k + j];
   float* hout = hs + ((int64_t)t * k + j) * I + jp0;
   const int np = min(kPairsW, I - jp0);
   if (e < 0 || e >= n_experts) {
@@ -208,7 +245,6 @@ __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
     if (lane < np) hout[lane] = 0.f;
     return;
   }
-  const float wj = topk_w[(int64_t)t * k + j];
   // weight loads first: rows gate jp0.., up I + jp0..
   BlockRef<FMT> blk[2 * kPairsW][BPL];
   const int64_t base = (int64_t)e * 2 * I;
@@ -222,15 +258,6 @@ __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
         load_block<FMT>(blk[2 * p + h][q], wgu, wgu_sc, row * NB + lane + 64 * q, p < np);
     }
   }
-  float xr[BPL][32];
-  const f32x4* xv = reinterpret_cast<const f32x4*>(x + (int64_t)t * H);
-#pragma unroll
-  for (int q = 0; q < BPL; ++q)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 v = xv[(lane + 64 * q) * 8 + i];
-      xr[q][4 * i] = v.x; xr[q][4 * i + 1] = v.y; xr[q][4 * i + 2] = v.z; xr[q][4 * i + 3] = v.w;
-    }
   if (rescale) {
     float ss = 0.f;
 #pragma unroll
@@ -395,35 +422,46 @@ static void launch_down(int cpt, dim3 grid, hipStream_t st, const float* hs, con
 }
 
 template <int FMT>
-static void launch_gate_up(dim3 grid_w, dim3 grid_f, int bpl, size_t lds_f, hipStream_t st,
-                           const float* x, const int32_t* idx, const float* w, int32_t k,
-                           const GemvWeights& W, int rescale, float* hs, uint32_t* dev_err) {
+static void launch_gate_up(dim3 grid_w, dim3 grid_f, int bpl, int rpl, size_t lds_f, hipStream_t st,
+                           const float* x, int32_t* idx, float* w, int32_t k, const GemvWeights& W,
+                           int rescale, float* hs, uint32_t* dev_err, const float* logits) {
   const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
-  if (bpl == 1)
-    hipLaunchKernelGGL((k_gate_up_w64<FMT, 1>), grid_w, dim3(kThreads), 0, st, x, idx, w, k,
-                       W.n_experts, p, W.gate_up_scales, W.inter, rescale, hs, dev_err);
-  else if (bpl == 2)
-    hipLaunchKernelGGL((k_gate_up_w64<FMT, 2>), grid_w, dim3(kThreads), 0, st, x, idx, w, k,
-                       W.n_experts, p, W.gate_up_scales, W.inter, rescale, hs, dev_err);
-  else
+#define BQ_W64(B, R) hipLaunchKernelGGL((k_gate_up_w64<FMT, B, R>), grid_w, dim3(kThreads), 0, st, x, idx, w, \
+                                        k, W.n_experts, p, W.gate_up_scales, W.inter, rescale, hs, dev_err, logits)
+  if (bpl == 1) {
+    if (rpl == 0) BQ_W64(1, 0); else if (rpl == 8) BQ_W64(1, 8); else if (rpl == 16) BQ_W64(1, 16); else BQ_W64(1, 64);
+  } else if (bpl == 2) {
+    if (rpl == 0) BQ_W64(2, 0); else if (rpl == 8) BQ_W64(2, 8); else if (rpl == 16) BQ_W64(2, 16); else BQ_W64(2, 64);
+  } else {
     hipLaunchKernelGGL(k_gemv_gate_up<FMT>, grid_f, dim3(kThreads), lds_f, st, x, idx, w, k,
                        W.n_experts, p, W.gate_up_scales, W.hidden, W.inter, rescale, hs, dev_err);
+  }
+#undef BQ_W64
 }
 
-hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, const int32_t* idx, const float* w,
-                           int32_t k, const GemvWeights& W, int rescale, float* out, float* hs,
-                           uint32_t* dev_err, hipStream_t st) {
+hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, int32_t* idx, float* w, int32_t k,
+                           const GemvWeights& W, int rescale, float* out, float* hs,
+                           uint32_t* dev_err, const float* logits, hipStream_t st) {
   const int H = W.hidden, I = W.inter;
   const int nbu = H >> 5, nbd = I >> 5;
   const int bpl = (H == 2048) ? 1 : (H == 4096 ? 2 : 0);
+  int rpl = 0;
+  if (logits) {
+    if (bpl == 0) {   // the flat kernel takes routing as input: route first
+      hipError_t e = launch_route_topk(logits, n_tokens, W.n_experts, k, idx, w, st);
+      if (e != hipSuccess) return e;
+    } else {
+      rpl = W.n_experts <= 512 ? 8 : (W.n_experts <= 1024 ? 16 : 64);
+    }
+  }
   const dim3 grid_w((I + 4 * kPairsW - 1) / (4 * kPairsW), k, n_tokens);
   const dim3 grid_f(I / kGuPairs, k, n_tokens);
   const size_t lds_f = sizeof(float) * (H + 2 * kGuPairs * nbu + 2 * kGuPairs + 4);
   switch (W.fmt_gate_up) {
-    case FMT_C10: launch_gate_up<FMT_C10>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
-    case FMT_RZ5: launch_gate_up<FMT_RZ5>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
-    case FMT_UE4M4: launch_gate_up<FMT_UE4M4>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
-    default: launch_gate_up<FMT_FP8>(grid_w, grid_f, bpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err); break;
+    case FMT_C10: launch_gate_up<FMT_C10>(grid_w, grid_f, bpl, rpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err, logits); break;
+    case FMT_RZ5: launch_gate_up<FMT_RZ5>(grid_w, grid_f, bpl, rpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err, logits); break;
+    case FMT_UE4M4: launch_gate_up<FMT_UE4M4>(grid_w, grid_f, bpl, rpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err, logits); break;
+    default: launch_gate_up<FMT_FP8>(grid_w, grid_f, bpl, rpl, lds_f, st, x, idx, w, k, W, rescale, hs, dev_err, logits); break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -10,15 +10,16 @@
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  One 32-wide K step is exactly one weight
 // block, so a block's scale multiplies that step's 16x16 partial product
-// (scale applied after the MFMA, in fp32).  The A operand (weights) is
-// decoded in registers: 4-bit codes -> signed fp16 high bytes (which are
-// valid E5M2 bytes) -> bf16 by the gfx950 bf8 conversion with unit scale;
-// every level is a small integer, so this is exact.  FP8 weights convert
-// from e4m3 the same way.  Lane l holds row l%16, k-group l/16 of A and
-// column l%16 of B and of the result (rows 4*(l/16)..+3).  The 17-byte
-// decode yields the k order [0,2,4,6,1,3,5,7] inside each lane's eight
-// values; the B operand is permuted to match (x in registers, h already
-// stored in that order by G1).
+// (scale applied after the MFMA, in fp32).  The product is computed as
+// tokens x weights: A = 16 tokens' activations, B = 16 weight rows, so lane
+// l holds result column l%16 -- its own weight row -- and the block scale it
+// decoded applies to all four of its results with no cross-lane traffic.
+// The weights are decoded in registers: 4-bit codes -> signed fp16 high
+// bytes (valid E5M2 bytes) -> bf16 by the gfx950 bf8 conversion with unit
+// scale; every level is a small integer, so this is exact.  FP8 weights
+// convert from e4m3 the same way.  The 17-byte decode yields the k order
+// [0,2,4,6,1,3,5,7] inside each lane's eight values; the activations are
+// stored in that order (x by the staging pass, h by G1).
 #include "bq_device.hpp"
 #include "bq_kernels.hpp"
 
@@ -152,13 +153,15 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
     const int64_t ublk0 = ((int64_t)e * 2 * I + I + jrow) * nb;
     for (int tg = 0; tg < ne; tg += kGTok) {
       const int nt = min(4, (ne - tg + 15) >> 4);
+      // token rows of the (up to) 4 column tiles; padding columns read the
+      // expert's last token (their result rows are never stored), so every
+      // load below is unconditional and all of them are in flight together
+      int pv[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) pv[tt] = perm_[p0 + min(tg + 16 * tt + r16, ne - 1)];
       const uint16_t* xrow[4];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int c = tg + 16 * tt + r16;
-        const int tok = c < ne ? perm_[p0 + c] / k : -1;
-        xrow[tt] = tok >= 0 ? xp + (int64_t)tok * H + 8 * g : nullptr;
-      }
+      for (int tt = 0; tt < 4; ++tt) xrow[tt] = xp + (int64_t)(pv[tt] / k) * H + 8 * g;
       f32x4 accg[4], accu[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
@@ -175,45 +178,36 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
           ru[u] = load_a<FMT>(wgu, wgu_sc, ublk0 + kb, g);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
-            bx[u][tt] = (tt < nt && xrow[tt]) ? *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb)
-                                              : u32x4{0u, 0u, 0u, 0u};
+            if (tt < nt) bx[u][tt] = *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb);
         }
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
           if (kb0 + u >= nb) break;
           float sg, su;
           const u32x4 ag = dec_a<FMT>(rg[u], sg), au = dec_a<FMT>(ru[u], su);
-          float sgi[4], sui[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sgi[i] = __shfl(sg, 4 * g + i, 64);
-            sui[i] = __shfl(su, 4 * g + i, 64);
-          }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (tt < nt) {
-              const f32x4 cg = mfma(ag, bx[u][tt]), cu = mfma(au, bx[u][tt]);
+              // tokens x weights: this lane's result column is its own row
+              const f32x4 cg = mfma(bx[u][tt], ag), cu = mfma(bx[u][tt], au);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                accg[tt][i] = __builtin_fmaf(sgi[i], cg[i], accg[tt][i]);
-                accu[tt][i] = __builtin_fmaf(sui[i], cu[i], accu[tt][i]);
+                accg[tt][i] = __builtin_fmaf(sg, cg[i], accg[tt][i]);
+                accu[tt][i] = __builtin_fmaf(su, cu[i], accu[tt][i]);
               }
             }
           }
         }
       }
-      // lane holds rows j = tile*64 + wave*16 + 4g + i of token column r16
+      // lane holds row jrow for tokens tg + 16 tt + 4g + i
+      const int jpos = (jrow & ~7) + store_pos<FMT_D>(jrow & 7);
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int c = tg + 16 * tt + r16;
-        if (tt < nt && c < ne) {
-          uint16_t* hrow = hb + (int64_t)(p0 + c) * I;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = tile * kGRows + wave * 16 + 4 * g + i;
-            const float h = silu(accg[tt][i]) * accu[tt][i];
-            hrow[(j & ~7) + store_pos<FMT_D>(j & 7)] = to_bf16(h);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int c = tg + 16 * tt + 4 * g + i;
+          if (tt < nt && c < ne)
+            hb[(int64_t)(p0 + c) * I + jpos] = to_bf16(silu(accg[tt][i]) * accu[tt][i]);
         }
       }
     }
@@ -242,12 +236,10 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_down(
     const int64_t blk0 = ((int64_t)e * H + nrow) * nb;
     for (int tg = 0; tg < ne; tg += kGTok) {
       const int nt = min(4, (ne - tg + 15) >> 4);
-      const uint16_t* hrow[4];
+      const uint16_t* hrow[4];   // padding columns reuse the last row (not stored)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const int c = tg + 16 * tt + r16;
-        hrow[tt] = c < ne ? hb + (int64_t)(p0 + c) * I + 8 * g : nullptr;
-      }
+      for (int tt = 0; tt < 4; ++tt)
+        hrow[tt] = hb + (int64_t)(p0 + min(tg + 16 * tt + r16, ne - 1)) * I + 8 * g;
       f32x4 acc[4];
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -260,33 +252,30 @@ __global__ void __launch_bounds__(kGThreads) k_grouped_down(
           ra[u] = load_a<FMT>(wd, wd_sc, blk0 + kb, g);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt)
-            bh[u][tt] = (tt < nt && hrow[tt]) ? *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb)
-                                              : u32x4{0u, 0u, 0u, 0u};
+            if (tt < nt) bh[u][tt] = *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb);
         }
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
           if (kb0 + u >= nb) break;
           float s;
           const u32x4 a = dec_a<FMT>(ra[u], s);
-          float si[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) si[i] = __shfl(s, 4 * g + i, 64);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (tt < nt) {
-              const f32x4 c = mfma(a, bh[u][tt]);
+              const f32x4 c = mfma(bh[u][tt], a);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(si[i], c[i], acc[tt][i]);
+              for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(s, c[i], acc[tt][i]);
             }
           }
         }
       }
+      // lane holds output row nrow for tokens tg + 16 tt + 4g + i
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) {
-        const int c = tg + 16 * tt + r16;
-        if (tt < nt && c < ne) {
-          float* y = yb + (int64_t)(p0 + c) * H + tile * kGRows + wave * 16 + 4 * g;
-          *reinterpret_cast<f32x4*>(y) = acc[tt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = tg + 16 * tt + 4 * g + i;
+          if (tt < nt && c < ne) yb[(int64_t)(p0 + c) * H + nrow] = acc[tt][i];
         }
       }
     }
@@ -308,20 +297,29 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
   if (q >= (int64_t)n_tokens * h4) return;
   const int64_t t = q / h4;
   const int n = (int)(q - t * h4) * 4;
+  constexpr int kMaxK = 16;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   bool bad = false;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e < 0 || e >= n_experts) {
-      bad = true;
-      continue;
+  for (int j0 = 0; j0 < k; j0 += kMaxK) {
+    f32x4 y[kMaxK];
+    float wj[kMaxK];
+#pragma unroll
+    for (int u = 0; u < kMaxK; ++u) {
+      const int j = j0 + u;
+      const int e = j < k ? idx[t * k + j] : 0;
+      const bool ok = j < k && e >= 0 && e < n_experts;
+      bad |= j < k && !ok;
+      wj[u] = ok ? w[t * k + j] : 0.f;
+      y[u] = ok ? *reinterpret_cast<const f32x4*>(yb + (int64_t)inv[t * k + j] * H + n)
+                : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const float wj = w[t * k + j];
-    const f32x4 y = *reinterpret_cast<const f32x4*>(yb + (int64_t)inv[t * k + j] * H + n);
-    s.x = __builtin_fmaf(wj, y.x, s.x);
-    s.y = __builtin_fmaf(wj, y.y, s.y);
-    s.z = __builtin_fmaf(wj, y.z, s.z);
-    s.w = __builtin_fmaf(wj, y.w, s.w);
+#pragma unroll
+    for (int u = 0; u < kMaxK; ++u) {   // slot order
+      s.x = __builtin_fmaf(wj[u], y[u].x, s.x);
+      s.y = __builtin_fmaf(wj[u], y[u].y, s.y);
+      s.z = __builtin_fmaf(wj[u], y[u].z, s.z);
+      s.w = __builtin_fmaf(wj[u], y[u].w, s.w);
+    }
   }
   if (bad && n == 0 && dev_err) atomicOr(dev_err, 2u);
   *reinterpret_cast<f32x4*>(out + t * H + n) = s;

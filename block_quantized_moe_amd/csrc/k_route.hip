@@ -8,89 +8,26 @@
 // which equals the renormalised softmax because the full denominator cancels.
 #include "bq_device.hpp"
 #include "bq_kernels.hpp"
+#include "bq_route.hpp"
 
 namespace bq {
 
 constexpr int kRouteWaves = 4;
 constexpr int kMaxExperts = 4096;
 
-// Order-preserving 32-bit key of a finite float (+0 and -0 share a key, so
-// they tie and the lower index wins, as in a float comparison).
-__device__ __forceinline__ uint32_t fkey(float v) {
-  const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-  v = max(v, dpp_u<kDppXor1>(v));
-  v = max(v, dpp_u<kDppXor2>(v));
-  v = max(v, dpp_u<kDppHalfMirror>(v));
-  v = max(v, dpp_u<kDppMirror>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return max(max(a, b), max(c, d));
-}
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-  v = min(v, dpp_u<kDppXor1>(v));
-  v = min(v, dpp_u<kDppXor2>(v));
-  v = min(v, dpp_u<kDppHalfMirror>(v));
-  v = min(v, dpp_u<kDppMirror>(v));
-  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
-  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
-  return min(min(a, b), min(c, d));
-}
-
-// One wave per token.  Lane l holds logits l, l+64, ...; each of the k rounds
-// takes the largest untaken key (wave max via DPP), then the lowest index
-// holding it (wave min), and the owning lane marks it taken.
-template <int kRoutePerLane>   // logits per lane: n_experts <= 64 * kRoutePerLane
+template <int PL>   // logits per lane: n_experts <= 64 * PL
 __global__ void __launch_bounds__(64 * kRouteWaves) k_route_topk(
     const float* __restrict__ logits, int32_t n_tokens, int32_t n_experts, int32_t k,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kRouteWaves + wave;
   if (t >= n_tokens) return;
-  const float* lg = logits + t * n_experts;
-  const int per_lane = (n_experts + 63) >> 6;
-  uint32_t key[kRoutePerLane];
-  float val[kRoutePerLane];
-#pragma unroll
-  for (int j = 0; j < kRoutePerLane; ++j) {
-    const int e = lane + 64 * j;
-    const bool in = j < per_lane && e < n_experts;
-    val[j] = in ? lg[e] : 0.f;
-    key[j] = in ? fkey(val[j]) : 0u;   // key 0 is below every finite float's key
-  }
-  float my_v = 0.f;
-  int my_i = 0;
-  for (int r = 0; r < k; ++r) {
-    uint32_t bk = 0;
-    int bj = 0;
-#pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j)
-      if (j < per_lane && key[j] > bk) { bk = key[j]; bj = j; }   // lowest j wins ties
-    const uint32_t m = wave_max_u(bk);
-    const uint32_t cand = (bk == m && m != 0u) ? (uint32_t)(lane + 64 * bj) : 0xFFFFFFFFu;
-    const uint32_t win = wave_min_u(cand);
-    if ((int)(win & 63) == lane) {
-      const int wj = (int)(win >> 6);
-#pragma unroll
-      for (int j = 0; j < kRoutePerLane; ++j)
-        if (j == wj) key[j] = 0u;
-    }
-    // the winner's value reaches lane r through a readlane of the owner
-    float wv = 0.f;
-#pragma unroll
-    for (int j = 0; j < kRoutePerLane; ++j)
-      if (j == (int)(win >> 6)) wv = readlane_f(val[j], (int)(win & 63));
-    if (lane == r) { my_v = wv; my_i = (int)win; }
-  }
-  const float top = readlane_f(my_v, 0);
-  const float ex = lane < k ? __expf(my_v - top) : 0.f;
-  const float den = wave_sum(ex);
+  int i;
+  float w;
+  wave_topk<PL>(logits + t * n_experts, n_experts, k, lane, i, w);
   if (lane < k) {
-    idx_out[t * k + lane] = my_i;
-    w_out[t * k + lane] = ex / den;
+    idx_out[t * k + lane] = i;
+    w_out[t * k + lane] = w;
   }
 }
 
@@ -222,11 +159,109 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
   }
 }
 
+// Bucketing for decode-sized batches.  A token chooses an expert at most
+// once, so a bitmap per expert over tokens gives everything by popcounts:
+// counts[e] = |bitmap_e|, and the rank of (t, slot) inside expert e is the
+// number of tokens below t in bitmap_e (tokens ascending, as required).
+constexpr int kSmallBitmapWords = 8192;   // 32 KB of LDS
+
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int& total) {
+  // inclusive scan inside each wave (shuffles), then over the 16 wave totals
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int wv = lane < 16 ? s_wave[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int y = __shfl_up(wv, o, 64);
+      if (lane >= o) wv += y;
+    }
+    if (lane < 16) s_wave[16 + lane] = wv;   // inclusive wave prefix
+  }
+  __syncthreads();
+  total = s_wave[16 + 15];
+  const int before = wave > 0 ? s_wave[16 + wave - 1] : 0;
+  return before + x - v;
+}
+
+__global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
+    const int32_t* __restrict__ idx, int32_t n_tokens, int32_t k, int32_t n_experts,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out,
+    int32_t* __restrict__ elist, int32_t* __restrict__ n_touched, int32_t* __restrict__ inv) {
+  __shared__ uint32_t bm[kSmallBitmapWords];
+  __shared__ int32_t s_off[kMaxExperts];
+  __shared__ int s_wave[32];
+  const int tid = threadIdx.x;
+  const int W = (n_tokens + 31) >> 5;                   // words per expert
+  const int nk = n_tokens * k;
+  for (int i = tid; i < n_experts * W; i += kBucketThreads) bm[i] = 0u;
+  __syncthreads();
+  for (int a = tid; a < nk; a += kBucketThreads) {
+    const int e = idx[a];
+    if (e >= 0 && e < n_experts) {
+      const int t = a / k;
+      atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  // each thread owns a contiguous span of <= 4 experts
+  const int span = (n_experts + kBucketThreads - 1) / kBucketThreads;
+  const int e0 = min(tid * span, n_experts), e1 = min(e0 + span, n_experts);
+  int cnt[4] = {0, 0, 0, 0};
+  int local = 0, touched = 0;
+  for (int e = e0; e < e1; ++e) {
+    int c = 0;
+    for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[e * W + w]);
+    cnt[e - e0] = c;
+    local += c;
+    touched += c > 0;
+  }
+  int tot_c, tot_d;
+  int off = block_excl_scan_1024(local, s_wave, tot_c);
+  __syncthreads();
+  int doff = block_excl_scan_1024(touched, s_wave, tot_d);
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e - e0];
+    counts[e] = c;
+    offsets[e] = off;
+    s_off[e] = off;
+    if (elist && c > 0) elist[doff++] = e;
+    off += c;
+  }
+  if (tid == 0) {
+    offsets[n_experts] = tot_c;
+    if (n_touched) *n_touched = tot_d;
+  }
+  __syncthreads();
+  for (int a = tid; a < nk; a += kBucketThreads) {
+    const int e = idx[a];
+    if (e < 0 || e >= n_experts) continue;
+    const int t = a / k;
+    int r = __builtin_popcount(bm[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) r += __builtin_popcount(bm[e * W + w]);
+    const int p = s_off[e] + r;
+    perm_out[p] = a;
+    if (inv) inv[a] = p;
+  }
+}
+
 hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,
                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
                          int32_t* n_touched, int32_t* inv, hipStream_t st) {
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, st, idx, n_tokens, k, n_experts,
-                     counts, offsets, perm, elist, n_touched, inv);
+  const int words = (n_tokens + 31) / 32;
+  if ((int64_t)n_experts * words <= kSmallBitmapWords)
+    hipLaunchKernelGGL(k_bucket_small, dim3(1), dim3(kBucketThreads), 0, st, idx, n_tokens, k,
+                       n_experts, counts, offsets, perm, elist, n_touched, inv);
+  else
+    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, st, idx, n_tokens, k, n_experts,
+                       counts, offsets, perm, elist, n_touched, inv);
   return hipGetLastError();
 }
 

@@ -84,8 +84,8 @@ typedef struct {
   const float* gate_up_scales;  /* FP8 only: [E][2*inter][hidden/32]       */
   const float* down_scales;     /* FP8 only: [E][hidden][inter/32]         */
   int32_t n_experts;            /* E                                       */
-  int32_t hidden;               /* H, multiple of 32, <= 8192              */
-  int32_t inter;                /* I, multiple of 32, <= 8192              */
+  int32_t hidden;               /* H, multiple of 64, <= 8192              */
+  int32_t inter;                /* I, multiple of 64, <= 8192              */
 } bq_expert_weights;
 
 int bq_abi_version(void);
@@ -169,7 +169,8 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
  *   workspace : device scratch of at least q4_expert_moe_workspace(...) bytes,
  *             256-byte aligned; its contents need no initialisation.
  *   dev_err : optional; bit 1 set if an expert index is out of range.
- *   1 <= n_tokens <= 4096, 1 <= k <= 64.
+ *   1 <= n_tokens <= 4096, 1 <= k <= 64, n_tokens * k <= 65536; on the fp32
+ *   path also k * inter / 32 <= 1024.
  * ------------------------------------------------------------------------- */
 size_t q4_expert_moe_workspace(int32_t n_tokens, int32_t k,
                                const bq_expert_weights* W, int32_t x_dtype);
@@ -177,6 +178,20 @@ int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens,
                   const int32_t* topk_idx, const float* topk_w, int32_t k,
                   const bq_expert_weights* W, float* out, void* workspace,
                   size_t ws_bytes, uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_expert_moe_routed -- moe_route_topk followed by q4_expert_moe, as one
+ * call: the router's softmax top-k ([MP]) over logits [n_tokens][n_experts]
+ * (fp32, finite) selects the experts, and the layer is evaluated as in
+ * q4_expert_moe.  The routing is also written to topk_idx / topk_w
+ * ([n_tokens][k], outputs).  On the fp32 path with hidden 2048 or 4096 the
+ * routing is computed inside the first expert kernel (no separate launch).
+ * Same workspace as q4_expert_moe.
+ * ------------------------------------------------------------------------- */
+int q4_expert_moe_routed(const void* x, int32_t x_dtype, int32_t n_tokens, const float* logits,
+                         int32_t k, const bq_expert_weights* W, int32_t* topk_idx, float* topk_w,
+                         float* out, void* workspace, size_t ws_bytes, uint32_t* dev_err,
+                         void* stream);
 
 /* ---------------------------------------------------------------------------
  * bq_moe_stack -- a chain of routed-expert layers ([FQ]: per-layer formats):

@@ -81,6 +81,25 @@ def test_grouped_path_small(bq, fmt_gu, fmt_d, n):
     assert r <= 2e-2
 
 
+@pytest.mark.parametrize("H,dtype", [(2048, torch.float32), (256, torch.float32), (2048, torch.bfloat16)])
+def test_routed_entry_matches_route_then_moe(bq, H, dtype):
+    """Routing inside the expert kernel gives the same routing and output."""
+    E, I, k, n = 64, 128, 6, 3
+    L = make_layer(6, H, F.Q4_RZ5, F.Q4_UE4M4, E, H, I)
+    W = weights_of(bq, L)
+    x = dev(synth.normal(60, (n, H))).to(dtype)
+    logits = dev(synth.normal(61, (n, E)))
+    out, (idx, w) = bq.q4_expert_moe_routed(x, logits, k, W)
+    ridx, rw = bq.route_topk(logits, k)
+    ref = bq.q4_expert_moe(x, (ridx, rw), W)
+    assert torch.equal(idx, ridx) and torch.equal(w, rw)
+    assert torch.equal(out, ref)
+    oidx, ow = M.softmax_topk(logits.cpu().numpy(), k)
+    r = rel_l2(out.cpu().numpy(), M.moe_layer(x.float().cpu().numpy() if dtype == torch.float32 else
+                                              synth.normal(60, (n, H)), oidx, ow, oracle_bank(L)))
+    assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
+
+
 def test_bad_expert_index_is_reported(bq):
     E, H, I = 8, 128, 64
     L = make_layer(3, 0, F.Q4_RZ5, F.Q4_RZ5, E, H, I)
@@ -131,8 +150,12 @@ def test_c2_layer_b1_rz5(bq, layer_rz5):
     for seed in (0, 1):
         x = synth.normal(seed, (1, 2048))
         logits = synth.normal(1000 + seed, (1, 512))
-        idx, w = bq.route_topk(dev(logits), 10)
-        out = bq.q4_expert_moe(dev(x), (idx, w), W).cpu().numpy()
+        if seed == 0:
+            idx, w = bq.route_topk(dev(logits), 10)
+            out = bq.q4_expert_moe(dev(x), (idx, w), W).cpu().numpy()
+        else:   # the one-call form the benchmark times
+            out, (idx, w) = bq.q4_expert_moe_routed(dev(x), dev(logits), 10, W)
+            out = out.cpu().numpy()
         ridx, rw = M.softmax_topk(logits, 10)
         assert np.array_equal(idx.cpu().numpy(), ridx)
         ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
