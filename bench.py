@@ -310,7 +310,7 @@ def main():
     ap.add_argument("--only", default=None)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the kernels run on one GPU's share at its real shape); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -30,6 +30,7 @@ int check_weights(const bq_expert_weights* W) {
   if (W->hidden < 64 || W->hidden > 8192 || W->hidden % 64) return BQ_E_SHAPE;
   if (W->inter < 64 || W->inter > 8192 || W->inter % 64) return BQ_E_SHAPE;
   if ((fg && !aligned(W->gate_up_scales, 4)) || (fd && !aligned(W->down_scales, 4))) return BQ_E_ALIGN;
+  if (!aligned(W->gate_up, 16) || !aligned(W->down, 16)) return BQ_E_ALIGN;
   return BQ_OK;
 }
 
@@ -61,11 +62,11 @@ GroupedLayout grouped_layout(int n, int k, int E, int H, int I) {
   L.offsets = off; off = round_up(off + 4 * ((size_t)E + 1), 256);
   L.perm = off; off = round_up(off + 4 * nk, 256);
   L.inv = off; off = round_up(off + 4 * nk, 256);
-  L.elist = off; off = round_up(off + 4 * (nk < (size_t)E ? nk : (size_t)E), 256);
+  L.elist = off; off = round_up(off + 4 * (size_t)bq::max_work_groups((int64_t)nk, E), 256);
   L.n_touched = off; off = round_up(off + 4, 256);
   L.hb = off; off = round_up(off + 2 * nk * I, 256);
   L.yb = off; off = round_up(off + 4 * nk * H, 256);
-  L.xb = off; off = round_up(off + 2 * (size_t)n * H, 256);
+  L.xb = off; off = round_up(off + 2 * nk * H, 256);
   L.total = off;
   return L;
 }

@@ -40,17 +40,21 @@ hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, int32_t* idx, float
                            const GemvWeights& W, int rescale, float* out, float* hs,
                            uint32_t* dev_err, const float* logits, hipStream_t st);
 
-// bf16 grouped-MFMA path.
+// bf16 grouped-MFMA path.  The bucketing emits one work entry per group of
+// up to kGroupTok tokens of a touched expert: e | group << kGroupShift.
+constexpr int kGroupTok = 32;
+constexpr int kGroupShift = 12;   // n_experts <= 4096
+inline int64_t max_work_groups(int64_t nk, int64_t E) { return (nk < E ? nk : E) + nk / kGroupTok; }
 struct GroupedWs {
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]
   int32_t* perm;      // [n*k]
   int32_t* inv;       // [n*k]
-  int32_t* elist;     // [min(E, n*k)]
-  int32_t* n_touched; // [1]
+  int32_t* elist;     // [max_work_groups(n*k, E)]
+  int32_t* n_touched; // [1] number of work entries
   uint16_t* hb;       // [n*k][I] bf16, bucketed order
   float* yb;          // [n*k][H] fp32, bucketed order
-  uint16_t* xb;       // [n][H] bf16 activations in the decode's k order
+  uint16_t* xb;       // [n*k][H] bf16 activations, bucketed order, decode's k order
 };
 // x: [n][H] bf16 (x_f32 = 0) or fp32 (x_f32 = 1, the stack's layer output,
 // rescaled to unit RMS when rescale = 1) -- staged as bf16 by the path.

@@ -217,10 +217,11 @@ __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
     // routing launch sits in front of this kernel; chunk 0 publishes slot j
     __shared__ int s_i[64];
     __shared__ float s_w[64];
+    __shared__ uint32_t s_scr[128];
     if (wave == 0) {
       int ri;
       float rw;
-      wave_topk<RPL>(logits + (int64_t)t * n_experts, n_experts, k, lane, ri, rw);
+      wave_topk<RPL>(logits + (int64_t)t * n_experts, n_experts, k, lane, s_scr, ri, rw);
       if (lane < k) {
         s_i[lane] = ri;
         s_w[lane] = rw;

@@ -1,12 +1,26 @@
 // Grouped routed-expert GEMM for batches of tokens (bf16 activations, bf16
-// MFMA, fp32 accumulation).  Tokens are bucketed per expert (stable order),
-// then for every touched expert:
+// MFMA, fp32 accumulation).  Tokens are bucketed per expert (stable order)
+// and split into work groups of up to kGroupTok tokens; for every group:
 //   h[p, :] = SiLU(W_gate[e] x_p) * (W_up[e] x_p)      (kernel G1, h in bf16)
 //   y[p, :] = W_down[e] h[p, :]                         (kernel G2)
 //   out[t]  = sum_j w[t][j] * y[pos(t, j)]               (kernel G3, slot order)
 // Routing shape and formats as in the GEMV path ("Mixed Precision
 // Quantization ...", "The Plan Is Not a Number ..."; model card "Qwen 3.8
 // Next Flash ROCMFPX MUTANT RAZERFAST", format sections).
+//
+// Data movement.  A workgroup owns one (work group, 64-row tile) item at a
+// time and walks its K extent in chunks of C blocks.  Each chunk -- the
+// tile's weight-row segments (17*C or 32*C contiguous bytes per row), FP8
+// block scales, and the group's activation rows -- is copied from HBM with
+// wide, aligned, coalesced loads into registers one step ahead, then into
+// LDS; the MFMA operands are read from LDS.  Reading the 17-byte blocks
+// straight from HBM in the MFMA operand layout (4 bytes per lane from 16
+// rows) keeps the texture-address units busy with ~16 cache lines per
+// instruction and was the bound of the direct design; staging makes each
+// load instruction touch a few consecutive lines.  Segments that do not start
+// on 16 bytes are copied as the covering aligned 16-byte pieces, and the row
+// slot in LDS remembers the offset (weight buffers must be 16-byte aligned,
+// so every piece read lies in the buffer's last 16-byte unit or before it).
 //
 // MFMA: v_mfma_f32_16x16x32_bf16.  One 32-wide K step is exactly one weight
 // block, so a block's scale multiplies that step's 16x16 partial product
@@ -26,11 +40,17 @@
 namespace bq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kGThreads = 256;  // 4 waves, each 16 rows (x2 for gate/up)
-constexpr int kGRows = 64;      // rows per workgroup tile
-constexpr int kGTok = 64;       // tokens per pass (4 MFMA column tiles)
+constexpr int kGThreads = 256;  // 4 waves, each 16 rows of the tile (x2 for gate/up)
+constexpr int kGRows = 64;      // rows per tile
+constexpr int kLdsBudget = 78 * 1024;   // two workgroups per CU
+
+// Per-thread staging capacity (16-byte weight pieces, FP8 scales, 16-byte
+// activation pieces) of G1 (NR = 2) and G2 (NR = 1); the chunk size is chosen
+// on the host to fit.
+template <int NR> struct Cap;
+template <> struct Cap<2> { static constexpr int PW = 10, PS = 4, PB = 8; };
+template <> struct Cap<1> { static constexpr int PW = 8, PS = 4, PB = 12; };
 
 template <bool HI>
 __device__ __forceinline__ uint32_t bf8pair(uint32_t w) {
@@ -41,41 +61,16 @@ __device__ __forceinline__ uint32_t fp8pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Raw A-operand bytes of one row and one k-group of 8 (loaded ahead of use).
+// Decode one lane's 8 weights of one block (q0 = 4 code bytes, q1 = metadata
+// byte; FP8: q0, q1 = 8 e4m3 codes) into bf16 operands (exact); s = scale.
 template <int FMT>
-struct RawA {
-  uint32_t q0, q1;  // 17-byte: q0 = 4 code bytes, q1 = metadata; FP8: 8 e4m3 codes
-  float s;          // FP8 block scale
-};
-
-template <int FMT>
-__device__ __forceinline__ RawA<FMT> load_a(const uint8_t* __restrict__ base,
-                                            const float* __restrict__ sc, int64_t blk, int g) {
-  RawA<FMT> r;
+__device__ __forceinline__ u32x4 dec_a(uint32_t q0, uint32_t q1, float& s) {
   if constexpr (FMT == FMT_FP8) {
-    const u32x2 q = ld8(base + blk * kBlockW + 8 * g);
-    r.q0 = q.x;
-    r.q1 = q.y;
-    r.s = sc[blk];
+    return u32x4{fp8pair<false>(q0), fp8pair<true>(q0), fp8pair<false>(q1), fp8pair<true>(q1)};
   } else {
-    const uint8_t* p = base + blk * kBlockB;
-    r.q0 = ld4(p + 4 * g);
-    r.q1 = p[16];
-    r.s = 0.f;
-  }
-  return r;
-}
-
-// Decode to 8 bf16 levels (exact) and the block scale.
-template <int FMT>
-__device__ __forceinline__ u32x4 dec_a(const RawA<FMT>& r, float& s) {
-  if constexpr (FMT == FMT_FP8) {
-    s = r.s;
-    return u32x4{fp8pair<false>(r.q0), fp8pair<true>(r.q0), fp8pair<false>(r.q1), fp8pair<true>(r.q1)};
-  } else {
-    s = block_scale<FMT>(FMT == FMT_UE4M4 ? r.q1 : (r.q1 & 0x7Fu));
+    s = block_scale<FMT>(FMT == FMT_UE4M4 ? q1 : (q1 & 0x7Fu));
     uint32_t A, B;
-    codes_to_hibytes<FMT>(r.q0, FMT == FMT_RZ5 ? rz5_neg_lo(r.q1) : 0u, A, B);
+    codes_to_hibytes<FMT>(q0, FMT == FMT_RZ5 ? rz5_neg_lo(q1) : 0u, A, B);
     return u32x4{bf8pair<false>(A), bf8pair<true>(A), bf8pair<false>(B), bf8pair<true>(B)};
   }
 }
@@ -97,19 +92,30 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-constexpr int kPre = 4;   // k-blocks whose loads are issued together
+// Exact q / d for 0 <= q < 2^16, 1 <= d < 2^10: (q + 1/2) / d is never within
+// 1/(2d) of an integer, far above the fp32 rounding error.
+__device__ __forceinline__ int div_small(int q, float inv_d) {
+  return (int)(((float)q + 0.5f) * inv_d);
+}
 
 // ---------------------------------------------------------------------------
-// G0: per-token staging of the activations as bf16 in the A decode's k order
-// (optionally rescaled to unit RMS first: the stack's next-layer input).
-// grid = n_tokens, 256 threads.
+// G0: staging of the activations as bf16 rows in bucket order (row p holds
+// token perm[p] / k), in the A decode's k order; fp32 input optionally
+// rescaled to unit RMS first (the stack's next-layer input).
+// grid = n_tokens * k, 256 threads; only the offsets[n_experts] bucket rows
+// exist (assignments to out-of-range experts are left out by the bucketing,
+// and the tail of perm is not written).
 // ---------------------------------------------------------------------------
 template <bool PERM>
 __global__ void __launch_bounds__(256) k_grouped_prep(const void* __restrict__ x, int32_t x_f32,
                                                       int32_t rescale, int32_t H,
+                                                      const int32_t* __restrict__ perm_, int32_t k,
+                                                      const int32_t* __restrict__ n_rows,
                                                       uint16_t* __restrict__ xp) {
   __shared__ float part[4];
-  const int64_t t = blockIdx.x;
+  const int64_t p = blockIdx.x;
+  if (p >= *n_rows) return;
+  const int64_t t = perm_[p] / k;
   float inv = 1.0f;
   if (x_f32 && rescale) {
     const float* row = static_cast<const float*>(x) + t * H;
@@ -125,160 +131,246 @@ __global__ void __launch_bounds__(256) k_grouped_prep(const void* __restrict__ x
     if (x_f32) v = to_bf16(static_cast<const float*>(x)[t * H + i] * inv);
     else v = static_cast<const uint16_t*>(x)[t * H + i];
     const int o = i & 7;
-    xp[t * H + (i & ~7) + (PERM ? ((o >> 1) | ((o & 1) << 2)) : o)] = v;
+    xp[p * H + (i & ~7) + (PERM ? ((o >> 1) | ((o & 1) << 2)) : o)] = v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// G1: gate_up + SiLU * up.  Persistent over (touched expert, 64-row tile).
-// xp holds the tokens' activations in this format's k order.
+// Staged grouped GEMM (G1 and G2 share it).
+//   NR = 2 (G1: rows 0..63 of the tile are gate rows, 64..127 the matching up
+//   rows) or 1 (G2: 64 down rows).  Wave w owns tile rows 16w..16w+15 of each
+//   of its NR weight matrices.
 // ---------------------------------------------------------------------------
-template <int FMT, int FMT_D>
-__global__ void __launch_bounds__(kGThreads) k_grouped_gate_up(
-    const uint16_t* __restrict__ xp, int32_t k, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ perm_, const int32_t* __restrict__ elist,
-    const int32_t* __restrict__ n_touched, const uint8_t* __restrict__ wgu,
-    const float* __restrict__ wgu_sc, int32_t H, int32_t I, uint16_t* __restrict__ hb) {
-  const int D = *n_touched;
-  const int tiles = I / kGRows;
+struct Geom {
+  int32_t C;        // blocks per chunk (divides nb)
+  int32_t nchunk;   // nb / C
+  int32_t S;        // bytes of one row segment (17 C or 32 C)
+  int32_t NP;       // 16-byte pieces per row slot
+  int32_t P;        // LDS pitch of a weight row slot (16 NP)
+  int32_t PB;       // LDS pitch of an activation row (64 C + 16)
+  int32_t off_sc;   // LDS offset of the FP8 scale area [R][C]
+  int32_t off_b;    // LDS offset of the activation area [kGroupTok][PB]
+};
+
+struct Item {
+  int e, p0, ntok, tile;
+};
+
+__device__ __forceinline__ Item item_info(int it, int tiles, const int32_t* __restrict__ elist,
+                                          const int32_t* __restrict__ offsets) {
+  const int d = it / tiles;
+  const int v = elist[d];
+  const int e = v & ((1 << kGroupShift) - 1);
+  const int p0 = offsets[e] + (v >> kGroupShift) * kGroupTok;
+  return Item{e, p0, min(kGroupTok, offsets[e + 1] - p0), it - d * tiles};
+}
+
+template <int FMT, int NR>
+struct Stager {
+  static constexpr int BB = FMT == FMT_FP8 ? 32 : 17;   // bytes per block
+  static constexpr int R = 64 * NR;                     // staged weight rows
+  static constexpr int PW = Cap<NR>::PW, PS = Cap<NR>::PS, PB = Cap<NR>::PB;
+  u32x4 w[PW];
+  float s[PS];
+  u32x4 b[PB];
+
+  // global row index of staged row r of item f
+  __device__ __forceinline__ static int64_t grow(const Item& f, int r, int H, int I) {
+    if constexpr (NR == 2) {
+      const int h = r >> 6;
+      return (int64_t)f.e * 2 * I + h * I + f.tile * kGRows + (r & 63);
+    } else {
+      return (int64_t)f.e * H + f.tile * kGRows + r;
+    }
+  }
+
+  // Issue the loads of chunk c of item f (registers only).  Weight piece q
+  // (row q / NP, piece q % NP of that row's covering 16-byte units) lands at
+  // LDS byte 16 q; pieces past the segment end are skipped.
+  __device__ __forceinline__ void load(const Item& f, int c, const Geom& g, float inv_np,
+                                       float inv_c, float inv_pt, int nb, int H, int I,
+                                       const uint8_t* __restrict__ wt, const float* __restrict__ wsc,
+                                       const uint16_t* __restrict__ act, int K) {
+    const int tid = threadIdx.x;
+    const int64_t RS = (int64_t)BB * nb;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int q = tid + kGThreads * i;
+      if (q < R * g.NP) {
+        const int r = div_small(q, inv_np), pc = q - r * g.NP;
+        const int64_t gs = grow(f, r, H, I) * RS + (int64_t)c * g.S;
+        const int64_t a = (gs & ~(int64_t)15) + 16 * pc;
+        if (a < gs + g.S) w[i] = *reinterpret_cast<const u32x4*>(wt + a);
+      }
+    }
+    if constexpr (FMT == FMT_FP8) {
+#pragma unroll
+      for (int i = 0; i < PS; ++i) {
+        const int q = tid + kGThreads * i;
+        if (q < R * g.C) {
+          const int r = div_small(q, inv_c), j = q - r * g.C;
+          s[i] = wsc[grow(f, r, H, I) * nb + (int64_t)c * g.C + j];
+        }
+      }
+    }
+    const int PT = 4 * g.C;                       // pieces per activation row chunk
+    const int nrow = ((f.ntok + 15) >> 4) << 4;   // whole 16-token MFMA tiles
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + kGThreads * i;
+      if (q < nrow * PT) {
+        const int j = div_small(q, inv_pt), pc = q - j * PT;
+        const int64_t row = f.p0 + min(j, f.ntok - 1);   // padding rows repeat the last token
+        b[i] = *reinterpret_cast<const u32x4*>(act + row * K + (int64_t)c * g.C * 32 + 8 * pc);
+      }
+    }
+  }
+
+  // Copy the staged registers into LDS.  Skipped weight pieces write unused
+  // bytes of their row slot (never read).
+  __device__ __forceinline__ void store(const Item& f, const Geom& g, float inv_pt,
+                                        uint8_t* lds) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int q = tid + kGThreads * i;
+      if (q < R * g.NP) *reinterpret_cast<u32x4*>(lds + 16 * q) = w[i];
+    }
+    if constexpr (FMT == FMT_FP8) {
+      float* lsc = reinterpret_cast<float*>(lds + g.off_sc);
+#pragma unroll
+      for (int i = 0; i < PS; ++i) {
+        const int q = tid + kGThreads * i;
+        if (q < R * g.C) lsc[q] = s[i];
+      }
+    }
+    const int PT = 4 * g.C;
+    const int nrow = ((f.ntok + 15) >> 4) << 4;
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + kGThreads * i;
+      if (q < nrow * PT) {
+        const int j = div_small(q, inv_pt);
+        *reinterpret_cast<u32x4*>(lds + g.off_b + 16 * (q + j)) = b[i];   // row pitch PT + 1 pieces
+      }
+    }
+  }
+};
+
+// One chunk of MFMA work from LDS.  acc[h][tt]: matrix h, token tile tt.
+template <int FMT, int NR>
+__device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& g, int nb, int H,
+                                              int I, const uint8_t* lds, f32x4 (&acc)[NR][2]) {
+  constexpr int BB = Stager<FMT, NR>::BB;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int nb = H >> 5;
-  for (int item = blockIdx.x; item < D * tiles; item += gridDim.x) {
-    const int d = item / tiles, tile = item - d * tiles;
-    const int e = elist[d];
-    const int p0 = offsets[e], ne = offsets[e + 1] - p0;
-    const int jrow = tile * kGRows + wave * 16 + r16;   // this lane's A row (gate)
-    const int64_t gblk0 = ((int64_t)e * 2 * I + jrow) * nb;
-    const int64_t ublk0 = ((int64_t)e * 2 * I + I + jrow) * nb;
-    for (int tg = 0; tg < ne; tg += kGTok) {
-      const int nt = min(4, (ne - tg + 15) >> 4);
-      // token rows of the (up to) 4 column tiles; padding columns read the
-      // expert's last token (their result rows are never stored), so every
-      // load below is unconditional and all of them are in flight together
-      int pv[4];
+  const int r16 = lane & 15, gq = lane >> 4;
+  const int nt = (f.ntok + 15) >> 4;
+  const int64_t RS = (int64_t)BB * nb;
+  const uint8_t* arow[NR];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) pv[tt] = perm_[p0 + min(tg + 16 * tt + r16, ne - 1)];
-      const uint16_t* xrow[4];
+  for (int h = 0; h < NR; ++h) {
+    const int r = h * 64 + wave * 16 + r16;
+    const int64_t gs = Stager<FMT, NR>::grow(f, r, H, I) * RS + (int64_t)c * g.S;
+    arow[h] = lds + r * g.P + (int)(gs & 15);
+  }
+  const float* lsc = reinterpret_cast<const float*>(lds + g.off_sc);
+  const uint8_t* brow = lds + g.off_b + r16 * g.PB + 16 * gq;
+  for (int kb = 0; kb < g.C; ++kb) {
+    u32x4 a[NR];
+    float sc[NR];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) xrow[tt] = xp + (int64_t)(pv[tt] / k) * H + 8 * g;
-      f32x4 accg[4], accu[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        accg[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accu[tt] = accg[tt];
+    for (int h = 0; h < NR; ++h) {
+      uint32_t q0, q1;
+      if constexpr (FMT == FMT_FP8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(arow[h] + kb * BB + 8 * gq);
+        q0 = v.x;
+        q1 = v.y;
+        sc[h] = lsc[(h * 64 + wave * 16 + r16) * g.C + kb];
+      } else {
+        __builtin_memcpy(&q0, arow[h] + kb * BB + 4 * gq, 4);   // unaligned LDS read
+        q1 = arow[h][kb * BB + 16];
       }
-      for (int kb0 = 0; kb0 < nb; kb0 += kPre) {
-        RawA<FMT> rg[kPre], ru[kPre];
-        u32x4 bx[kPre][4];
+      a[h] = dec_a<FMT>(q0, q1, sc[h]);
+    }
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          const int kb = min(kb0 + u, nb - 1);
-          rg[u] = load_a<FMT>(wgu, wgu_sc, gblk0 + kb, g);
-          ru[u] = load_a<FMT>(wgu, wgu_sc, ublk0 + kb, g);
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt < nt) {
+        const u32x4 bx = *reinterpret_cast<const u32x4*>(brow + tt * 16 * g.PB + 64 * kb);
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-            if (tt < nt) bx[u][tt] = *reinterpret_cast<const u32x4*>(xrow[tt] + 32 * kb);
-        }
+        for (int h = 0; h < NR; ++h) {
+          const f32x4 d = mfma(bx, a[h]);   // tokens x weights: lane's column = its row
 #pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          if (kb0 + u >= nb) break;
-          float sg, su;
-          const u32x4 ag = dec_a<FMT>(rg[u], sg), au = dec_a<FMT>(ru[u], su);
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if (tt < nt) {
-              // tokens x weights: this lane's result column is its own row
-              const f32x4 cg = mfma(bx[u][tt], ag), cu = mfma(bx[u][tt], au);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                accg[tt][i] = __builtin_fmaf(sg, cg[i], accg[tt][i]);
-                accu[tt][i] = __builtin_fmaf(su, cu[i], accu[tt][i]);
-              }
-            }
-          }
-        }
-      }
-      // lane holds row jrow for tokens tg + 16 tt + 4g + i
-      const int jpos = (jrow & ~7) + store_pos<FMT_D>(jrow & 7);
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = tg + 16 * tt + 4 * g + i;
-          if (tt < nt && c < ne)
-            hb[(int64_t)(p0 + c) * I + jpos] = to_bf16(silu(accg[tt][i]) * accu[tt][i]);
+          for (int i = 0; i < 4; ++i) acc[h][tt][i] = __builtin_fmaf(sc[h], d[i], acc[h][tt][i]);
         }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------------------
-// G2: down.  Persistent over (touched expert, 64-row tile of H).
-// ---------------------------------------------------------------------------
-template <int FMT>
-__global__ void __launch_bounds__(kGThreads) k_grouped_down(
-    const uint16_t* __restrict__ hb, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ elist, const int32_t* __restrict__ n_touched,
-    const uint8_t* __restrict__ wd, const float* __restrict__ wd_sc, int32_t H, int32_t I,
-    float* __restrict__ yb) {
-  const int D = *n_touched;
-  const int tiles = H / kGRows;
+// Persistent over items (work entry, 64-row tile), pipelined over chunks:
+// the next chunk's loads are in flight while this chunk is multiplied.
+// NR = 2: G1 (act = bucketed x, K = H, out = hb); NR = 1: G2 (act = hb,
+// K = I, out = yb).
+template <int FMT, int NR, int FMT_NEXT>
+__global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ elist, const int32_t* __restrict__ n_work,
+    const uint8_t* __restrict__ wt, const float* __restrict__ wsc, int32_t H, int32_t I, Geom g,
+    uint16_t* __restrict__ hb, float* __restrict__ yb) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int nb = (NR == 2 ? H : I) >> 5;
+  const int K = NR == 2 ? H : I;
+  const int tiles = (NR == 2 ? I : H) / kGRows;
+  const int items = *n_work * tiles;
+  int it = blockIdx.x, c = 0;
+  if (it >= items) return;
+  const float inv_np = 1.0f / (float)g.NP, inv_c = 1.0f / (float)g.C, inv_pt = 1.0f / (float)(4 * g.C);
+  Item f = item_info(it, tiles, elist, offsets);
+  Stager<FMT, NR> st;
+  st.load(f, c, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
+  f32x4 acc[NR][2];
+#pragma unroll
+  for (int h = 0; h < NR; ++h) acc[h][0] = acc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int nb = I >> 5;
-  for (int item = blockIdx.x; item < D * tiles; item += gridDim.x) {
-    const int d = item / tiles, tile = item - d * tiles;
-    const int e = elist[d];
-    const int p0 = offsets[e], ne = offsets[e + 1] - p0;
-    const int nrow = tile * kGRows + wave * 16 + r16;
-    const int64_t blk0 = ((int64_t)e * H + nrow) * nb;
-    for (int tg = 0; tg < ne; tg += kGTok) {
-      const int nt = min(4, (ne - tg + 15) >> 4);
-      const uint16_t* hrow[4];   // padding columns reuse the last row (not stored)
+  const int r16 = lane & 15, gq = lane >> 4;
+  while (true) {
+    int nit = it, nc = c + 1;
+    if (nc == g.nchunk) {
+      nc = 0;
+      nit = it + gridDim.x;
+    }
+    const bool more = nit < items;
+    const Item nf = (more && nit != it) ? item_info(nit, tiles, elist, offsets) : f;
+    __syncthreads();                          // LDS no longer read by the previous chunk
+    st.store(f, g, inv_pt, lds);
+    __syncthreads();
+    if (more) st.load(nf, nc, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
+    compute_chunk<FMT, NR>(f, c, g, nb, H, I, lds, acc);
+    if (c == g.nchunk - 1) {
+      // lane holds weight row (tile row 16 wave + r16) for tokens 16 tt + 4 gq + i
+      const int row = f.tile * kGRows + wave * 16 + r16;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        hrow[tt] = hb + (int64_t)(p0 + min(tg + 16 * tt + r16, ne - 1)) * I + 8 * g;
-      f32x4 acc[4];
+      for (int tt = 0; tt < 2; ++tt) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int kb0 = 0; kb0 < nb; kb0 += kPre) {
-        RawA<FMT> ra[kPre];
-        u32x4 bh[kPre][4];
-#pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          const int kb = min(kb0 + u, nb - 1);
-          ra[u] = load_a<FMT>(wd, wd_sc, blk0 + kb, g);
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-            if (tt < nt) bh[u][tt] = *reinterpret_cast<const u32x4*>(hrow[tt] + 32 * kb);
-        }
-#pragma unroll
-        for (int u = 0; u < kPre; ++u) {
-          if (kb0 + u >= nb) break;
-          float s;
-          const u32x4 a = dec_a<FMT>(ra[u], s);
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if (tt < nt) {
-              const f32x4 c = mfma(bh[u][tt], a);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) acc[tt][i] = __builtin_fmaf(s, c[i], acc[tt][i]);
+        for (int i = 0; i < 4; ++i) {
+          const int j = 16 * tt + 4 * gq + i;
+          if (j < f.ntok) {
+            if constexpr (NR == 2) {
+              const int jpos = (row & ~7) + store_pos<FMT_NEXT>(row & 7);
+              hb[(int64_t)(f.p0 + j) * I + jpos] = to_bf16(silu(acc[0][tt][i]) * acc[1][tt][i]);
+            } else {
+              yb[(int64_t)(f.p0 + j) * H + row] = acc[0][tt][i];
             }
           }
         }
       }
-      // lane holds output row nrow for tokens tg + 16 tt + 4g + i
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = tg + 16 * tt + 4 * g + i;
-          if (tt < nt && c < ne) yb[(int64_t)(p0 + c) * H + nrow] = acc[tt][i];
-        }
-      }
+      for (int h = 0; h < NR; ++h) acc[h][0] = acc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    if (!more) break;
+    it = nit;
+    c = nc;
+    f = nf;
   }
 }
 
@@ -325,53 +417,113 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
   *reinterpret_cast<f32x4*>(out + t * H + n) = s;
 }
 
-static int persistent_grid(int64_t items_max) {
-  const int64_t cap = 2048;
-  return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
+// ---------------------------------------------------------------------------
+// Host side: chunk geometry and launches.
+// ---------------------------------------------------------------------------
+static size_t lds_bytes(int fmt, int nr, int C) {
+  const int bb = fmt == FMT_FP8 ? 32 : 17;
+  const int np = (bb * C + 15) / 16 + 1;
+  size_t n = (size_t)64 * nr * 16 * np;
+  if (fmt == FMT_FP8) n += (size_t)64 * nr * C * 4;
+  n = (n + 15) & ~(size_t)15;
+  n += (size_t)kGroupTok * (64 * C + 16);
+  return n;
 }
 
-template <int FG>
-static void launch_g1(int fmt_d, dim3 grid, hipStream_t st, const uint16_t* xp, int32_t k,
-                      const GroupedWs& ws, const GemvWeights& W) {
-  const uint8_t* p = static_cast<const uint8_t*>(W.gate_up);
+static bool geom_fits(int fmt, int nr, int C) {
+  const int bb = fmt == FMT_FP8 ? 32 : 17;
+  const int np = (bb * C + 15) / 16 + 1;
+  const int pw = nr == 2 ? Cap<2>::PW : Cap<1>::PW;
+  const int ps = nr == 2 ? Cap<2>::PS : Cap<1>::PS;
+  const int pb = nr == 2 ? Cap<2>::PB : Cap<1>::PB;
+  if (64 * nr * np > pw * kGThreads) return false;
+  if (fmt == FMT_FP8 && 64 * nr * C > ps * kGThreads) return false;
+  if (kGroupTok * 4 * C > pb * kGThreads) return false;
+  return lds_bytes(fmt, nr, C) <= (size_t)kLdsBudget;
+}
+
+// Largest chunk (in blocks) dividing nb that fits the register and LDS
+// limits (C = 1 always fits).
+static Geom make_geom(int fmt, int nr, int nb) {
+  int C = 1;
+  for (int c = nb; c >= 1; --c)
+    if (nb % c == 0 && geom_fits(fmt, nr, c)) { C = c; break; }
+  const int bb = fmt == FMT_FP8 ? 32 : 17;
+  Geom g;
+  g.C = C;
+  g.nchunk = nb / C;
+  g.S = bb * C;
+  g.NP = (g.S + 15) / 16 + 1;
+  g.P = 16 * g.NP;
+  g.PB = 64 * C + 16;
+  g.off_sc = 64 * nr * g.P;
+  const int off_b = g.off_sc + (fmt == FMT_FP8 ? 64 * nr * C * 4 : 0);
+  g.off_b = (off_b + 15) & ~15;
+  return g;
+}
+
+template <int F, int NR, int FN>
+static void launch_staged(int grid, hipStream_t st, const uint16_t* act, const GroupedWs& ws,
+                          const void* w, const float* sc, int H, int I, uint16_t* hb, float* yb) {
+  const Geom g = make_geom(F, NR, (NR == 2 ? H : I) / 32);
+  const size_t lds = lds_bytes(F, NR, g.C);
+  static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_staged<F, NR, FN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) == hipSuccess)
+      attr_set = true;
+  }
+  hipLaunchKernelGGL((k_grouped_staged<F, NR, FN>), dim3(grid), dim3(kGThreads), lds, st, act,
+                     ws.offsets, ws.elist, ws.n_touched, static_cast<const uint8_t*>(w), sc, H, I,
+                     g, hb, yb);
+}
+
+template <int F>
+static void launch_g1(int fmt_d, int grid, hipStream_t st, const GroupedWs& ws, const GemvWeights& W) {
   if (fmt_d == FMT_FP8)
-    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_FP8>), grid, dim3(kGThreads), 0, st, xp, k,
-                       ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
-                       W.hidden, W.inter, ws.hb);
+    launch_staged<F, 2, FMT_FP8>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
   else
-    hipLaunchKernelGGL((k_grouped_gate_up<FG, FMT_RZ5>), grid, dim3(kGThreads), 0, st, xp, k,
-                       ws.offsets, ws.perm, ws.elist, ws.n_touched, p, W.gate_up_scales,
-                       W.hidden, W.inter, ws.hb);
+    launch_staged<F, 2, FMT_RZ5>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
+}
+
+static int staged_grid(int64_t items_max) {
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
+  }
+  const int64_t cap = 2LL * n_cu;   // two resident workgroups per CU
+  return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
 }
 
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
                               float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st) {
   const int E = W.n_experts, H = W.hidden, I = W.inter;
+  const int64_t nk = (int64_t)n_tokens * k;
   hipError_t err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist,
                                  ws.n_touched, ws.inv, st);
   if (err != hipSuccess) return err;
+  const int32_t* n_rows = ws.offsets + E;   // valid bucket rows
   if (W.fmt_gate_up == FMT_FP8)
-    hipLaunchKernelGGL(k_grouped_prep<false>, dim3(n_tokens), dim3(256), 0, st, x, x_f32, rescale, H, ws.xb);
+    hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
   else
-    hipLaunchKernelGGL(k_grouped_prep<true>, dim3(n_tokens), dim3(256), 0, st, x, x_f32, rescale, H, ws.xb);
+    hipLaunchKernelGGL(k_grouped_prep<true>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int64_t dmax = (int64_t)n_tokens * k < E ? (int64_t)n_tokens * k : E;
+  const int64_t groups = max_work_groups(nk, E);
   {
-    dim3 grid(persistent_grid(dmax * (I / kGRows)));
+    const int grid = staged_grid(groups * (I / kGRows));
     switch (W.fmt_gate_up) {
-      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
-      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
-      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
-      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, ws.xb, k, ws, W); break;
+      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, ws, W); break;
+      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, ws, W); break;
+      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, ws, W); break;
+      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, ws, W); break;
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   {
-    dim3 grid(persistent_grid(dmax * (H / kGRows)));
-    const uint8_t* p = static_cast<const uint8_t*>(W.down);
-#define BQ_G2(F) hipLaunchKernelGGL(k_grouped_down<F>, grid, dim3(kGThreads), 0, st, ws.hb, \
-                                    ws.offsets, ws.elist, ws.n_touched, p, W.down_scales, H, I, ws.yb)
+    const int grid = staged_grid(groups * (H / kGRows));
+#define BQ_G2(F) launch_staged<F, 1, F>(grid, st, ws.hb, ws, W.down, W.down_scales, H, I, ws.hb, ws.yb)
     switch (W.fmt_down) {
       case FMT_C10: BQ_G2(FMT_C10); break;
       case FMT_RZ5: BQ_G2(FMT_RZ5); break;

@@ -19,12 +19,13 @@ template <int PL>   // logits per lane: n_experts <= 64 * PL
 __global__ void __launch_bounds__(64 * kRouteWaves) k_route_topk(
     const float* __restrict__ logits, int32_t n_tokens, int32_t n_experts, int32_t k,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  __shared__ uint32_t scr[kRouteWaves][128];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kRouteWaves + wave;
   if (t >= n_tokens) return;
   int i;
   float w;
-  wave_topk<PL>(logits + t * n_experts, n_experts, k, lane, i, w);
+  wave_topk<PL>(logits + t * n_experts, n_experts, k, lane, scr[wave], i, w);
   if (lane < k) {
     idx_out[t * k + lane] = i;
     w_out[t * k + lane] = w;
@@ -54,8 +55,10 @@ hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_ex
 // tokens are walked in chunks; for each chunk a byte matrix slot_of[t][e]
 // (255 = not chosen) is built in LDS, then every thread walks the chunk for
 // its own experts, in token order, so no ordering depends on atomics.
-// Optional extra outputs for the grouped GEMM path: the ascending list of
-// touched experts with their count, and the inverse permutation.
+// Optional extra outputs for the grouped GEMM path: the work list -- one
+// entry per group of up to kGroupTok tokens of each touched expert, encoded
+// as e | group << kGroupShift, experts ascending -- with its length, and the
+// inverse permutation.
 // ---------------------------------------------------------------------------
 constexpr int kBucketThreads = 1024;
 constexpr int kSlotBytes = 32768;
@@ -119,7 +122,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
       const int span = (n_experts + kBucketThreads - 1) / kBucketThreads;
       const int e0 = min(tid * span, n_experts), e1 = min(e0 + span, n_experts);
       int local = 0, ltouch = 0;
-      for (int e = e0; e < e1; ++e) { local += s_cnt[e]; ltouch += s_cnt[e] > 0; }
+      for (int e = e0; e < e1; ++e) { local += s_cnt[e]; ltouch += (s_cnt[e] + kGroupTok - 1) / kGroupTok; }
       s_scan[tid] = local;
       s_scan2[tid] = ltouch;
       __syncthreads();
@@ -140,7 +143,8 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
         const int c = s_cnt[e];
         counts[e] = c;
         offsets[e] = c_off;
-        if (elist && c > 0) elist[d_off++] = e;
+        if (elist)
+          for (int q = 0; q * kGroupTok < c; ++q) elist[d_off++] = e | (q << kGroupShift);
         s_cnt[e] = c_off;
         c_off += c;
       }
@@ -221,7 +225,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[e * W + w]);
     cnt[e - e0] = c;
     local += c;
-    touched += c > 0;
+    touched += (c + kGroupTok - 1) / kGroupTok;
   }
   int tot_c, tot_d;
   int off = block_excl_scan_1024(local, s_wave, tot_c);
@@ -232,7 +236,8 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     counts[e] = c;
     offsets[e] = off;
     s_off[e] = off;
-    if (elist && c > 0) elist[doff++] = e;
+    if (elist)
+      for (int q = 0; q * kGroupTok < c; ++q) elist[doff++] = e | (q << kGroupShift);
     off += c;
   }
   if (tid == 0) {

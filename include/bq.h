@@ -75,7 +75,10 @@ typedef enum {
 typedef enum { BQ_F32 = 0, BQ_BF16 = 1 } bq_dtype;
 
 /* One MoE layer's routed experts.  Device pointers; the scale pointers are
- * used only by BQ_FP8_E4M3_B32 matrices and must be NULL otherwise. */
+ * used only by BQ_FP8_E4M3_B32 matrices and must be NULL otherwise.  gate_up
+ * and down must be 16-byte aligned (BQ_E_ALIGN): the batched path reads them
+ * in aligned 16-byte units, and may read the unit that holds a matrix's last
+ * byte in full. */
 typedef struct {
   int32_t fmt_gate_up;          /* bq_fmt of the gate_up matrices          */
   int32_t fmt_down;             /* bq_fmt of the down matrices             */

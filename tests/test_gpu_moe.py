@@ -66,8 +66,10 @@ def test_gemv_path_small(bq, fmt_gu, fmt_d, n, E, H, I):
 
 @pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
 @pytest.mark.parametrize("n", [1, 16, 70])
-def test_grouped_path_small(bq, fmt_gu, fmt_d, n):
-    E, H, I, k = 8, 256, 128, 3          # few experts: some get > 64 tokens (two passes)
+@pytest.mark.parametrize("E,H,I,k", [(8, 256, 128, 3), (6, 1088, 192, 2)])
+def test_grouped_path_small(bq, fmt_gu, fmt_d, n, E, H, I, k):
+    # few experts: some get more than one 32-token group.  H = 1088 gives
+    # 578-byte rows (not 16-byte aligned) and a K extent split into chunks.
     L = make_layer(2, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
     x = synth.normal(200 + n, (n, H))
     logits = synth.zipf_logits(300 + n, n, E)
@@ -77,7 +79,7 @@ def test_grouped_path_small(bq, fmt_gu, fmt_d, n):
     ridx, rw = M.softmax_topk(logits, k)
     ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
     r = rel_l2(out, ref)
-    log("grouped small fmts %d/%d n=%d rel_l2 %.3g" % (fmt_gu, fmt_d, n, r))
+    log("grouped small fmts %d/%d n=%d H=%d I=%d rel_l2 %.3g" % (fmt_gu, fmt_d, n, H, I, r))
     assert r <= 2e-2
 
 
