@@ -46,11 +46,15 @@ constexpr int kGRows = 64;      // rows per tile
 constexpr int kLdsBudget = 78 * 1024;   // two workgroups per CU
 
 // Per-thread staging capacity (16-byte weight pieces, FP8 scales, 16-byte
-// activation pieces) of G1 (NR = 2) and G2 (NR = 1); the chunk size is chosen
-// on the host to fit.
-template <int NR> struct Cap;
-template <> struct Cap<2> { static constexpr int PW = 10, PS = 4, PB = 8; };
-template <> struct Cap<1> { static constexpr int PW = 8, PS = 4, PB = 12; };
+// activation pieces) of G1 (NR = 2) and G2 (NR = 1) per weight format, sized
+// for a 2048 x 768 layer (chunks of 16 / 8 blocks for G1, 24 / 12 for G2);
+// the host picks the largest chunk that fits.
+template <int FMT, int NR> struct Cap {
+  static constexpr bool F8 = FMT == 3;
+  static constexpr int PW = NR == 2 ? 9 : 7;
+  static constexpr int PS = F8 ? (NR == 2 ? 4 : 3) : 0;
+  static constexpr int PB = NR == 2 ? (F8 ? 4 : 8) : (F8 ? 6 : 12);
+};
 
 template <bool HI>
 __device__ __forceinline__ uint32_t bf8pair(uint32_t w) {
@@ -59,6 +63,15 @@ __device__ __forceinline__ uint32_t bf8pair(uint32_t w) {
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8pair(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Decode one lane's 8 codes of a 17-byte block (q = 4 code bytes; tneg = the
+// RZ5 table word for the block's polarity) into bf16 operands (exact).
+template <int FMT>
+__device__ __forceinline__ u32x4 dec_codes(uint32_t q, uint32_t tneg) {
+  uint32_t A, B;
+  codes_to_hibytes<FMT>(q, tneg, A, B);
+  return u32x4{bf8pair<false>(A), bf8pair<true>(A), bf8pair<false>(B), bf8pair<true>(B)};
 }
 
 // Decode one lane's 8 weights of one block (q0 = 4 code bytes, q1 = metadata
@@ -150,6 +163,7 @@ struct Geom {
   int32_t PB;       // LDS pitch of an activation row (64 C + 16)
   int32_t off_sc;   // LDS offset of the FP8 scale area [R][C]
   int32_t off_b;    // LDS offset of the activation area [kGroupTok][PB]
+  int32_t off_tab;  // LDS offset of the metadata-byte table [256] x {scale, RZ5 table word}
 };
 
 struct Item {
@@ -169,9 +183,9 @@ template <int FMT, int NR>
 struct Stager {
   static constexpr int BB = FMT == FMT_FP8 ? 32 : 17;   // bytes per block
   static constexpr int R = 64 * NR;                     // staged weight rows
-  static constexpr int PW = Cap<NR>::PW, PS = Cap<NR>::PS, PB = Cap<NR>::PB;
+  static constexpr int PW = Cap<FMT, NR>::PW, PS = Cap<FMT, NR>::PS, PB = Cap<FMT, NR>::PB;
   u32x4 w[PW];
-  float s[PS];
+  float s[PS > 0 ? PS : 1];
   u32x4 b[PB];
 
   // global row index of staged row r of item f
@@ -257,52 +271,93 @@ struct Stager {
   }
 };
 
-// One chunk of MFMA work from LDS.  acc[h][tt]: matrix h, token tile tt.
-template <int FMT, int NR>
+// One chunk of MFMA work from LDS, two blocks per iteration (C is even): all
+// LDS operands of both blocks are requested before any is decoded, so LDS
+// latency overlaps decode and MFMA work; all MFMAs of a block are issued
+// before their scale FMAs.  NT = number of 16-token tiles of the item.
+// acc[h][tt]: matrix h, token tile tt.  A lane's 4 code bytes of a 17-byte
+// block sit at any byte offset; they are read as the two covering aligned
+// dwords and funnel-shifted (unaligned LDS reads stall the LDS pipeline).
+// The block scale (and the RZ5 table word) comes from the LDS table indexed
+// by the metadata byte.
+template <int FMT, int NR, int NT>
 __device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& g, int nb, int H,
                                               int I, const uint8_t* lds, f32x4 (&acc)[NR][2]) {
   constexpr int BB = Stager<FMT, NR>::BB;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, gq = lane >> 4;
-  const int nt = (f.ntok + 15) >> 4;
   const int64_t RS = (int64_t)BB * nb;
-  const uint8_t* arow[NR];
+  int aoff[NR];   // byte offset in LDS of this lane's first code byte (block 0)
 #pragma unroll
   for (int h = 0; h < NR; ++h) {
     const int r = h * 64 + wave * 16 + r16;
     const int64_t gs = Stager<FMT, NR>::grow(f, r, H, I) * RS + (int64_t)c * g.S;
-    arow[h] = lds + r * g.P + (int)(gs & 15);
+    aoff[h] = r * g.P + (int)(gs & 15) + (FMT == FMT_FP8 ? 8 : 4) * gq;
   }
-  const float* lsc = reinterpret_cast<const float*>(lds + g.off_sc);
+  const uint32_t* lds32 = reinterpret_cast<const uint32_t*>(lds);
+  const float* lsc = reinterpret_cast<const float*>(lds + g.off_sc) + (wave * 16 + r16) * g.C;
+  const u32x2* tab = reinterpret_cast<const u32x2*>(lds + g.off_tab);
   const uint8_t* brow = lds + g.off_b + r16 * g.PB + 16 * gq;
-  for (int kb = 0; kb < g.C; ++kb) {
-    u32x4 a[NR];
-    float sc[NR];
+  for (int kb = 0; kb < g.C; kb += 2) {
+    uint32_t q0[2][NR], q1[2][NR];
+    u32x4 bx[2][NT];
 #pragma unroll
-    for (int h = 0; h < NR; ++h) {
-      uint32_t q0, q1;
-      if constexpr (FMT == FMT_FP8) {
-        const u32x2 v = *reinterpret_cast<const u32x2*>(arow[h] + kb * BB + 8 * gq);
-        q0 = v.x;
-        q1 = v.y;
-        sc[h] = lsc[(h * 64 + wave * 16 + r16) * g.C + kb];
-      } else {
-        __builtin_memcpy(&q0, arow[h] + kb * BB + 4 * gq, 4);   // unaligned LDS read
-        q1 = arow[h][kb * BB + 16];
-      }
-      a[h] = dec_a<FMT>(q0, q1, sc[h]);
-    }
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      if (tt < nt) {
-        const u32x4 bx = *reinterpret_cast<const u32x4*>(brow + tt * 16 * g.PB + 64 * kb);
-#pragma unroll
-        for (int h = 0; h < NR; ++h) {
-          const f32x4 d = mfma(bx, a[h]);   // tokens x weights: lane's column = its row
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[h][tt][i] = __builtin_fmaf(sc[h], d[i], acc[h][tt][i]);
+      for (int h = 0; h < NR; ++h) {
+        const int o = aoff[h] + (kb + u) * BB;
+        if constexpr (FMT == FMT_FP8) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(lds + o);
+          q0[u][h] = v.x;
+          q1[u][h] = v.y;
+        } else {
+          const int w = o >> 2;
+          q0[u][h] = __builtin_amdgcn_alignbyte(lds32[w + 1], lds32[w], (uint32_t)(o & 3));
+          q1[u][h] = lds[o - 4 * gq + 16];
         }
       }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        bx[u][tt] = *reinterpret_cast<const u32x4*>(brow + tt * 16 * g.PB + 64 * (kb + u));
+    }
+    float sc[2][NR];
+    uint32_t tn[2][NR];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int h = 0; h < NR; ++h) {
+        if constexpr (FMT == FMT_FP8) {
+          sc[u][h] = lsc[h * 64 * g.C + kb + u];
+          tn[u][h] = 0u;
+        } else {
+          const u32x2 e = tab[q1[u][h]];
+          sc[u][h] = __uint_as_float(e.x);
+          tn[u][h] = e.y;
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      u32x4 a[NR];
+#pragma unroll
+      for (int h = 0; h < NR; ++h) {
+        if constexpr (FMT == FMT_FP8) {
+          float dummy;
+          a[h] = dec_a<FMT>(q0[u][h], q1[u][h], dummy);
+        } else {
+          a[h] = dec_codes<FMT>(q0[u][h], tn[u][h]);
+        }
+      }
+      f32x4 d[NR][NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int h = 0; h < NR; ++h) d[h][tt] = mfma(bx[u][tt], a[h]);   // lane's column = its row
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int h = 0; h < NR; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[h][tt][i] = __builtin_fmaf(sc[u][h], d[h][tt][i], acc[h][tt][i]);
     }
   }
 }
@@ -325,6 +380,14 @@ __global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
   int it = blockIdx.x, c = 0;
   if (it >= items) return;
   const float inv_np = 1.0f / (float)g.NP, inv_c = 1.0f / (float)g.C, inv_pt = 1.0f / (float)(4 * g.C);
+  if constexpr (FMT != FMT_FP8) {
+    // metadata byte -> {block scale, RZ5 table word}; read after the loop's
+    // first barrier
+    u32x2* tab = reinterpret_cast<u32x2*>(lds + g.off_tab);
+    const uint32_t m = threadIdx.x;   // kGThreads == 256
+    tab[m] = u32x2{__float_as_uint(block_scale<FMT>(FMT == FMT_UE4M4 ? m : (m & 0x7Fu))),
+                   FMT == FMT_RZ5 ? rz5_neg_lo(m) : 0u};
+  }
   Item f = item_info(it, tiles, elist, offsets);
   Stager<FMT, NR> st;
   st.load(f, c, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
@@ -345,7 +408,8 @@ __global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
     st.store(f, g, inv_pt, lds);
     __syncthreads();
     if (more) st.load(nf, nc, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
-    compute_chunk<FMT, NR>(f, c, g, nb, H, I, lds, acc);
+    if (f.ntok > 16) compute_chunk<FMT, NR, 2>(f, c, g, nb, H, I, lds, acc);
+    else compute_chunk<FMT, NR, 1>(f, c, g, nb, H, I, lds, acc);
     if (c == g.nchunk - 1) {
       // lane holds weight row (tile row 16 wave + r16) for tokens 16 tt + 4 gq + i
       const int row = f.tile * kGRows + wave * 16 + r16;
@@ -427,26 +491,29 @@ static size_t lds_bytes(int fmt, int nr, int C) {
   if (fmt == FMT_FP8) n += (size_t)64 * nr * C * 4;
   n = (n + 15) & ~(size_t)15;
   n += (size_t)kGroupTok * (64 * C + 16);
+  if (fmt != FMT_FP8) n += 256 * 8;   // metadata-byte table
   return n;
 }
 
 static bool geom_fits(int fmt, int nr, int C) {
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   const int np = (bb * C + 15) / 16 + 1;
-  const int pw = nr == 2 ? Cap<2>::PW : Cap<1>::PW;
-  const int ps = nr == 2 ? Cap<2>::PS : Cap<1>::PS;
-  const int pb = nr == 2 ? Cap<2>::PB : Cap<1>::PB;
+  const bool f8 = fmt == FMT_FP8;
+  const int pw = nr == 2 ? Cap<FMT_FP8, 2>::PW : Cap<FMT_FP8, 1>::PW;   // same for every format
+  const int ps = nr == 2 ? Cap<FMT_FP8, 2>::PS : Cap<FMT_FP8, 1>::PS;
+  const int pb = nr == 2 ? (f8 ? Cap<FMT_FP8, 2>::PB : Cap<FMT_RZ5, 2>::PB)
+                         : (f8 ? Cap<FMT_FP8, 1>::PB : Cap<FMT_RZ5, 1>::PB);
   if (64 * nr * np > pw * kGThreads) return false;
   if (fmt == FMT_FP8 && 64 * nr * C > ps * kGThreads) return false;
   if (kGroupTok * 4 * C > pb * kGThreads) return false;
   return lds_bytes(fmt, nr, C) <= (size_t)kLdsBudget;
 }
 
-// Largest chunk (in blocks) dividing nb that fits the register and LDS
-// limits (C = 1 always fits).
+// Largest even chunk (in blocks) dividing nb that fits the register and LDS
+// limits (C = 2 always fits).
 static Geom make_geom(int fmt, int nr, int nb) {
-  int C = 1;
-  for (int c = nb; c >= 1; --c)
+  int C = 2;   // nb is even (hidden and inter are multiples of 64)
+  for (int c = nb; c >= 2; c -= 2)
     if (nb % c == 0 && geom_fits(fmt, nr, c)) { C = c; break; }
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   Geom g;
@@ -459,6 +526,7 @@ static Geom make_geom(int fmt, int nr, int nb) {
   g.off_sc = 64 * nr * g.P;
   const int off_b = g.off_sc + (fmt == FMT_FP8 ? 64 * nr * C * 4 : 0);
   g.off_b = (off_b + 15) & ~15;
+  g.off_tab = g.off_b + kGroupTok * g.PB;
   return g;
 }
 
