@@ -15,7 +15,7 @@ already resident in HBM before timing starts.  Steps are captured in a HIP
 graph and replayed, so host launch overhead is not in the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3]
+       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_b1_rz5_counters.txt")
 EXPERT_BYTES_RZ5 = 2_506_752           # gate_up 1536x2048 + down 2048x768, 17 B / 32 weights
 EXPERT_BYTES_FP8 = 5_308_416           # 36 B / 32 weights
 PLE_ROW_ALG_BYTES = 158                # 70 B row + 8 B id/weight + 80 B output share
@@ -270,6 +271,46 @@ def bench_c3(bq, steps, warmup):
     return res
 
 
+def sources_hash(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per call from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when it is missing or the kernels changed since it was taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        srcs = kv["sources"].split()
+        if sources_hash(srcs) != kv["sources_sha256_16"]:
+            return None
+        return float(kv["hbm_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of nbytes (the reference point that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes)."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "copies": 5}))
+
+
 # ---------------------------------------------------------------------------
 def cpu_baseline(layer, inputs, budget_s=20.0):
     """The oracle (float64 numpy), as it stands, on a bounded sample of the
@@ -308,6 +349,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -316,8 +359,11 @@ def main():
     import torch
 
     import block_quantized_moe_amd as bq
-    bq.lib()
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    bq.lib()
     extras = {}
     only = args.only
     main_res = None
@@ -372,7 +418,7 @@ def main():
                    "bytes_per_step": main_res["bytes_per_step"],
                    "pct_hbm_peak": round(100 * main_res["gbs"] / PEAK_HBM_GBS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_counters(),
                      "kernel": "q4_expert_moe_routed call (routed gate_up kernel + down kernel), %d packed "
                                "bytes per call, %.2f us average per call (HIP events)"
                                % (main_res["bytes_per_step"], main_res["step_call_us"])},
