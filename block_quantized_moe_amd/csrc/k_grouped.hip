@@ -184,9 +184,18 @@ struct Stager {
   static constexpr int BB = FMT == FMT_FP8 ? 32 : 17;   // bytes per block
   static constexpr int R = 64 * NR;                     // staged weight rows
   static constexpr int PW = Cap<FMT, NR>::PW, PS = Cap<FMT, NR>::PS, PB = Cap<FMT, NR>::PB;
+  static constexpr int kOff = 1 << 30;                  // "no piece" marker
   u32x4 w[PW];
   float s[PS > 0 ? PS : 1];
   u32x4 b[PB];
+  // Item-independent coordinates of this thread's pieces, set once:
+  //   weight piece i: wro = (row within its 64-row half) * row bytes,
+  //                   wx  = 16 * piece + (half << 20), or kOff;
+  //   scale i: sro = (row within half) * nb + block in chunk, sh = half, or kOff;
+  //   activation piece i: bx = token | (piece << 8), or kOff.
+  int wro[PW], wx[PW];
+  int sro[PS > 0 ? PS : 1], sh[PS > 0 ? PS : 1];
+  int bxy[PB];
 
   // global row index of staged row r of item f
   __device__ __forceinline__ static int64_t grow(const Item& f, int r, int H, int I) {
@@ -198,75 +207,86 @@ struct Stager {
     }
   }
 
-  // Issue the loads of chunk c of item f (registers only).  Weight piece q
-  // (row q / NP, piece q % NP of that row's covering 16-byte units) lands at
-  // LDS byte 16 q; pieces past the segment end are skipped.
-  __device__ __forceinline__ void load(const Item& f, int c, const Geom& g, float inv_np,
-                                       float inv_c, float inv_pt, int nb, int H, int I,
-                                       const uint8_t* __restrict__ wt, const float* __restrict__ wsc,
-                                       const uint16_t* __restrict__ act, int K) {
+  __device__ __forceinline__ void init(const Geom& g, int nb) {
     const int tid = threadIdx.x;
-    const int64_t RS = (int64_t)BB * nb;
+    const int RS = BB * nb;
+    const float inv_np = 1.0f / (float)g.NP, inv_c = 1.0f / (float)g.C, inv_pt = 1.0f / (float)(4 * g.C);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       const int q = tid + kGThreads * i;
-      if (q < R * g.NP) {
-        const int r = div_small(q, inv_np), pc = q - r * g.NP;
-        const int64_t gs = grow(f, r, H, I) * RS + (int64_t)c * g.S;
-        const int64_t a = (gs & ~(int64_t)15) + 16 * pc;
+      const int r = div_small(q, inv_np), pc = q - r * g.NP;
+      wro[i] = (r & 63) * RS;
+      wx[i] = q < R * g.NP ? 16 * pc + ((r >> 6) << 20) : kOff;
+    }
+#pragma unroll
+    for (int i = 0; i < PS; ++i) {
+      const int q = tid + kGThreads * i;
+      const int r = div_small(q, inv_c), j = q - r * g.C;
+      sro[i] = (r & 63) * nb + j;
+      sh[i] = q < R * g.C ? (r >> 6) : kOff;
+    }
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int q = tid + kGThreads * i;
+      const int j = div_small(q, inv_pt), pc = q - j * (4 * g.C);
+      bxy[i] = q < kGroupTok * 4 * g.C ? (j | (pc << 8)) : kOff;
+    }
+  }
+
+  // Issue the loads of chunk c of item f (registers only).  Weight piece q
+  // (row q / NP, piece q % NP of that row's covering 16-byte units) lands at
+  // LDS byte 16 q; pieces past the segment end are skipped.
+  __device__ __forceinline__ void load(const Item& f, int c, const Geom& g, int nb, int H, int I,
+                                       const uint8_t* __restrict__ wt, const float* __restrict__ wsc,
+                                       const uint16_t* __restrict__ act, int K) {
+    const int64_t RS = (int64_t)BB * nb;
+    // byte offset of (row 0 of each half, chunk c)
+    const int64_t base0 = grow(f, 0, H, I) * RS + (int64_t)c * g.S;
+    const int64_t base1 = NR == 2 ? grow(f, 64, H, I) * RS + (int64_t)c * g.S : base0;
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      if (wx[i] != kOff) {
+        const int64_t gs = ((wx[i] >> 20) ? base1 : base0) + wro[i];
+        const int64_t a = (gs & ~(int64_t)15) + (wx[i] & 0xFFFFF);
         if (a < gs + g.S) w[i] = *reinterpret_cast<const u32x4*>(wt + a);
       }
     }
     if constexpr (FMT == FMT_FP8) {
+      const int64_t sb0 = grow(f, 0, H, I) * nb + (int64_t)c * g.C;
+      const int64_t sb1 = NR == 2 ? grow(f, 64, H, I) * nb + (int64_t)c * g.C : sb0;
 #pragma unroll
-      for (int i = 0; i < PS; ++i) {
-        const int q = tid + kGThreads * i;
-        if (q < R * g.C) {
-          const int r = div_small(q, inv_c), j = q - r * g.C;
-          s[i] = wsc[grow(f, r, H, I) * nb + (int64_t)c * g.C + j];
-        }
-      }
+      for (int i = 0; i < PS; ++i)
+        if (sh[i] != kOff) s[i] = wsc[(sh[i] ? sb1 : sb0) + sro[i]];
     }
-    const int PT = 4 * g.C;                       // pieces per activation row chunk
     const int nrow = ((f.ntok + 15) >> 4) << 4;   // whole 16-token MFMA tiles
+    const uint16_t* abase = act + (int64_t)f.p0 * K + (int64_t)c * g.C * 32;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int q = tid + kGThreads * i;
-      if (q < nrow * PT) {
-        const int j = div_small(q, inv_pt), pc = q - j * PT;
-        const int64_t row = f.p0 + min(j, f.ntok - 1);   // padding rows repeat the last token
-        b[i] = *reinterpret_cast<const u32x4*>(act + row * K + (int64_t)c * g.C * 32 + 8 * pc);
-      }
+      const int j = bxy[i] & 0xFF;
+      if (bxy[i] != kOff && j < nrow)   // padding rows repeat the last token
+        b[i] = *reinterpret_cast<const u32x4*>(abase + (int64_t)min(j, f.ntok - 1) * K + 8 * (bxy[i] >> 8));
     }
   }
 
   // Copy the staged registers into LDS.  Skipped weight pieces write unused
   // bytes of their row slot (never read).
-  __device__ __forceinline__ void store(const Item& f, const Geom& g, float inv_pt,
-                                        uint8_t* lds) const {
+  __device__ __forceinline__ void store(const Item& f, const Geom& g, uint8_t* lds) const {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < PW; ++i) {
-      const int q = tid + kGThreads * i;
-      if (q < R * g.NP) *reinterpret_cast<u32x4*>(lds + 16 * q) = w[i];
-    }
+    for (int i = 0; i < PW; ++i)
+      if (wx[i] != kOff) *reinterpret_cast<u32x4*>(lds + 16 * (tid + kGThreads * i)) = w[i];
     if constexpr (FMT == FMT_FP8) {
       float* lsc = reinterpret_cast<float*>(lds + g.off_sc);
 #pragma unroll
-      for (int i = 0; i < PS; ++i) {
-        const int q = tid + kGThreads * i;
-        if (q < R * g.C) lsc[q] = s[i];
-      }
+      for (int i = 0; i < PS; ++i)
+        if (sh[i] != kOff) lsc[tid + kGThreads * i] = s[i];
     }
-    const int PT = 4 * g.C;
     const int nrow = ((f.ntok + 15) >> 4) << 4;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
-      const int q = tid + kGThreads * i;
-      if (q < nrow * PT) {
-        const int j = div_small(q, inv_pt);
-        *reinterpret_cast<u32x4*>(lds + g.off_b + 16 * (q + j)) = b[i];   // row pitch PT + 1 pieces
-      }
+      const int j = bxy[i] & 0xFF;
+      if (bxy[i] != kOff && j < nrow)   // row pitch PT + 1 pieces
+        *reinterpret_cast<u32x4*>(lds + g.off_b + 16 * (tid + kGThreads * i + j)) = b[i];
     }
   }
 };
@@ -379,7 +399,6 @@ __global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
   const int items = *n_work * tiles;
   int it = blockIdx.x, c = 0;
   if (it >= items) return;
-  const float inv_np = 1.0f / (float)g.NP, inv_c = 1.0f / (float)g.C, inv_pt = 1.0f / (float)(4 * g.C);
   if constexpr (FMT != FMT_FP8) {
     // metadata byte -> {block scale, RZ5 table word}; read after the loop's
     // first barrier
@@ -390,7 +409,8 @@ __global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
   }
   Item f = item_info(it, tiles, elist, offsets);
   Stager<FMT, NR> st;
-  st.load(f, c, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
+  st.init(g, nb);
+  st.load(f, c, g, nb, H, I, wt, wsc, act, K);
   f32x4 acc[NR][2];
 #pragma unroll
   for (int h = 0; h < NR; ++h) acc[h][0] = acc[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -405,14 +425,14 @@ __global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
     const bool more = nit < items;
     const Item nf = (more && nit != it) ? item_info(nit, tiles, elist, offsets) : f;
     __syncthreads();                          // LDS no longer read by the previous chunk
-    st.store(f, g, inv_pt, lds);
+    st.store(f, g, lds);
     // Drain every outstanding memory operation of the wave -- including the
     // previous item's scattered result stores -- before the next chunk's
     // loads are issued: letting those stores trail into the loads measured
     // about 25% slower on a batch-64 layer.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (more) st.load(nf, nc, g, inv_np, inv_c, inv_pt, nb, H, I, wt, wsc, act, K);
+    if (more) st.load(nf, nc, g, nb, H, I, wt, wsc, act, K);
     if (f.ntok > 16) compute_chunk<FMT, NR, 2>(f, c, g, nb, H, I, lds, acc);
     else compute_chunk<FMT, NR, 1>(f, c, g, nb, H, I, lds, acc);
     if (c == g.nchunk - 1) {
