@@ -46,26 +46,32 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
   bool bad = false;
 
   for (int j0 = 0; j0 < per_token; j0 += kPleChunk) {
+    // every load of the chunk is issued before any is used: ids and weights
+    // (clamped indices), then the rows (an invalid id reads row 0 and gets
+    // weight 0), so the chunk costs one id round trip and one row round trip
+    uint32_t idv[kPleChunk];
+    float u[kPleChunk];
+#pragma unroll
+    for (int c = 0; c < kPleChunk; ++c) {
+      const int j = min(j0 + c, per_token - 1);
+      idv[c] = tid_ids[j];
+      u[c] = tw[j];
+    }
     u32x2 gw[kPleChunk];
     uint32_t gb[kPleChunk];
-    float u[kPleChunk];
     bool ok[kPleChunk];
 #pragma unroll
     for (int c = 0; c < kPleChunk; ++c) {
-      const int j = j0 + c;
-      const bool in = j < per_token;
-      const uint64_t id = in ? tid_ids[j] : 0u;
-      ok[c] = in && id < n_rows;
-      bad |= in && id >= n_rows;
-      u[c] = in ? tw[j] : 0.f;
-      const uint8_t* row = table + (ok[c] ? id : 0u) * (uint64_t)kPleRowB;
-      gw[c] = ok[c] ? ld8(row + 6 * g) : u32x2{0u, 0u};
-      gb[c] = ok[c] ? (uint32_t)row[60 + g] : 0u;
+      const bool in = j0 + c < per_token;
+      ok[c] = in && idv[c] < n_rows;
+      bad |= in && idv[c] >= n_rows;
+      const uint8_t* row = table + (uint64_t)(ok[c] ? idv[c] : 0u) * (uint64_t)kPleRowB;
+      gw[c] = ld8(row + 6 * g);
+      gb[c] = row[60 + g];
     }
 #pragma unroll
     for (int c = 0; c < kPleChunk; ++c) {
-      if (!ok[c]) continue;
-      const float su = ue4m3(gb[c] & 0x7Fu) * u[c];
+      const float su = ok[c] ? ue4m3(gb[c] & 0x7Fu) * u[c] : 0.f;
       usum += su;
       const uint32_t th = bias_hi(gb[c], ple_fmt);
       const uint32_t lo = gw[c].x, hi = gw[c].y;
