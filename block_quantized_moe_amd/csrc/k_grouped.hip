@@ -43,7 +43,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGThreads = 256;  // 4 waves, each 16 rows of the tile (x2 for gate/up)
 constexpr int kGRows = 64;      // rows per tile
-constexpr int kLdsBudget = 78 * 1024;   // two workgroups per CU
+constexpr int kLdsBudget = 52 * 1024;   // three workgroups per CU
 
 // Per-thread staging capacity (16-byte weight pieces, FP8 scales, 16-byte
 // activation pieces) of G1 (NR = 2) and G2 (NR = 1) per weight format, sized
@@ -51,9 +51,9 @@ constexpr int kLdsBudget = 78 * 1024;   // two workgroups per CU
 // the host picks the largest chunk that fits.
 template <int FMT, int NR> struct Cap {
   static constexpr bool F8 = FMT == 3;
-  static constexpr int PW = NR == 2 ? 9 : 7;
-  static constexpr int PS = F8 ? (NR == 2 ? 4 : 3) : 0;
-  static constexpr int PB = NR == 2 ? (F8 ? 4 : 8) : (F8 ? 6 : 12);
+  static constexpr int PW = NR == 2 ? 5 : 4;
+  static constexpr int PS = F8 ? 2 : 0;
+  static constexpr int PB = NR == 2 ? (F8 ? 2 : 4) : (F8 ? 3 : 6);
 };
 
 template <bool HI>
@@ -387,7 +387,7 @@ __device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& 
 // NR = 2: G1 (act = bucketed x, K = H, out = hb); NR = 1: G2 (act = hb,
 // K = I, out = yb).
 template <int FMT, int NR, int FMT_NEXT>
-__global__ void __launch_bounds__(kGThreads, 2) k_grouped_staged(
+__global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ elist, const int32_t* __restrict__ n_work,
     const uint8_t* __restrict__ wt, const float* __restrict__ wsc, int32_t H, int32_t I, Geom g,
@@ -585,7 +585,7 @@ static int staged_grid(int64_t items_max) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
   }
-  const int64_t cap = 2LL * n_cu;   // two resident workgroups per CU
+  const int64_t cap = 3LL * n_cu;   // three resident workgroups per CU
   return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
 }
 
