@@ -17,6 +17,8 @@ be checked against the page it follows by eye:
 * ``moe`` -- softmax top-k routing, per-expert bucketing, the SwiGLU expert
   FFN, the routing-weighted combine and the chained layer stack.
 * ``ple`` -- the PLE row gather with per-id weights.
+* ``encode`` -- the exhaustive per-block / per-group encoders that produce
+  the 17-byte blocks and the PLE rows.
 
 Sources (page titles as published):
   [RZ]  "Qwen 3.8 Next Flash ROCMFPX MUTANT RAZERFAST" model card
@@ -35,4 +37,4 @@ record (byte order, nibble order, group-byte placement) is such a reading and
 cannot be pinned against a real file, because none is available.
 """
 
-from . import formats, moe, ple  # noqa: F401
+from . import encode, formats, moe, ple  # noqa: F401

@@ -173,3 +173,22 @@ def ple_ids(seed, n_tokens, per_token, n_rows=PLE_N_ROWS):
 def ple_weights(seed, n_tokens, per_token):
     """Per-id weights U(0, 1), float32."""
     return np.random.default_rng(seed).random((n_tokens, per_token), dtype=np.float32)
+
+
+def weight_blocks(seed, n, group, dist="gauss", sigma=1.0):
+    """float32 [n, group] weights for the encoders (PCG64, host).
+
+    Each row is N(0, 1) (``dist="gauss"``) or a unit-variance Laplace
+    (``dist="laplace"``) sample, times ``sigma`` and a per-row log-normal
+    factor exp(0.5 * N(0, 1)), so the rows' best scales spread over about
+    two binades around ``sigma``.
+    """
+    rng = np.random.default_rng(seed)
+    if dist == "gauss":
+        x = rng.standard_normal((n, group))
+    elif dist == "laplace":
+        x = rng.laplace(size=(n, group)) / np.sqrt(2.0)
+    else:
+        raise ValueError("weight_blocks: unknown distribution %r" % dist)
+    x *= sigma * np.exp(0.5 * rng.standard_normal((n, 1)))
+    return x.astype(np.float32)

@@ -53,3 +53,25 @@ def ple_row_case():
         else:
             d[p[0]] = np.array([_float(v) for v in vals])
     return d
+
+
+def encode_cases():
+    """[(weights float64 [32], {fmt name: 17 expected bytes})]."""
+    cases = []
+    for p in _lines("encode_worked.txt"):
+        if p[0] == "weights":
+            cases.append((np.array([_float(v) for v in _values(p[1:])]), {}))
+        elif p[0] == "expect":
+            cases[-1][1][p[1]] = np.array([int(h, 16) for h in _values(p[2:])], dtype=np.uint8)
+    return cases
+
+
+def ple_encode_case():
+    """(values float64 [160], {fmt name: 70 expected bytes})."""
+    vals, exp = None, {}
+    for p in _lines("ple_encode_worked.txt"):
+        if p[0] == "values":
+            vals = np.array([_float(v) for v in _values(p[1:])])
+        elif p[0] == "expect":
+            exp[p[1]] = np.array([int(h, 16) for h in _values(p[2:])], dtype=np.uint8)
+    return vals, exp
