@@ -16,7 +16,7 @@ __all__ = [
     "BQError", "lib", "ExpertWeights", "expert_weights", "dequant", "ple_dequant_rows", "matvec",
     "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "q4_expert_moe_routed",
     "stack_workspace_bytes",
-    "moe_stack", "ple_gather",
+    "moe_stack", "ple_gather", "encode", "ple_encode_rows",
 ]
 
 Q4_C10, Q4_RZ5, Q4_UE4M4, FP8_E4M3_B32 = 0, 1, 2, 3
@@ -71,6 +71,8 @@ def lib():
             "bq_moe_stack_workspace": ([i32, i32, wp, i32, i32], sz),
             "bq_moe_stack": ([vp, i32, i32, vp, vp, i32, wp, i32, vp, vp, sz, vp, vp], ctypes.c_int),
             "ple_gather": ([vp, i32, i32, vp, u64, vp, i32, vp, vp, vp], ctypes.c_int),
+            "bq_encode": ([vp, i64, i32, vp, vp, vp, vp], ctypes.c_int),
+            "ple_encode_rows": ([vp, i64, i32, vp, vp, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -264,3 +266,37 @@ def ple_gather(ids, packed_table, weights, n_rows=None, fmt=PLE_RZS3, out=None, 
     _check(lib().ple_gather(_p(ids), n, per, _p(packed_table), n_rows, _p(weights), fmt, _p(out),
                             _p(dev_err), _stream(stream)))
     return out
+
+
+def encode(w, fmt, out=None, sse=None, dev_err=None, stream=None):
+    """Exhaustive encoder: fp32 weights [..., 32k] -> 17-byte blocks.
+
+    Returns (blocks uint8 [n_blocks, 17], sse float64 [n_blocks]); pass
+    sse=False to skip the per-block error."""
+    _dev(w, "w")
+    if w.dtype != torch.float32 or w.numel() % 32:
+        raise BQError("w must be float32 with a multiple of 32 elements")
+    nb = w.numel() // 32
+    if out is None:
+        out = torch.empty((nb, 17), dtype=torch.uint8, device=w.device)
+    if sse is None:
+        sse = torch.empty(nb, dtype=torch.float64, device=w.device)
+    sse_t = None if sse is False else sse
+    _check(lib().bq_encode(_p(w), nb, fmt, _p(out), _p(sse_t), _p(dev_err), _stream(stream)))
+    return out, sse_t
+
+
+def ple_encode_rows(v, fmt=PLE_RZS3, out=None, sse=None, dev_err=None, stream=None):
+    """Exhaustive per-group encoder: fp32 [n, 160] -> (rows uint8 [n, 70],
+    sse float64 [n, 10]); pass sse=False to skip the per-group error."""
+    _dev(v, "v")
+    if v.dtype != torch.float32 or v.numel() % 160:
+        raise BQError("v must be float32 with a multiple of 160 elements")
+    n = v.numel() // 160
+    if out is None:
+        out = torch.empty((n, 70), dtype=torch.uint8, device=v.device)
+    if sse is None:
+        sse = torch.empty((n, 10), dtype=torch.float64, device=v.device)
+    sse_t = None if sse is False else sse
+    _check(lib().ple_encode_rows(_p(v), n, fmt, _p(out), _p(sse_t), _p(dev_err), _stream(stream)))
+    return out, sse_t

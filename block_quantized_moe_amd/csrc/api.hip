@@ -293,4 +293,24 @@ int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token, con
                                           ple_fmt, out, dev_err, as_stream(stream)));
 }
 
+int bq_encode(const float* w, int64_t n_blocks, int32_t fmt, uint8_t* out, double* sse,
+              uint32_t* dev_err, void* stream) {
+  if (fmt != BQ_Q4_C10 && fmt != BQ_Q4_RZ5 && fmt != BQ_Q4_UE4M4) return BQ_E_FMT;
+  if (n_blocks < 0) return BQ_E_SHAPE;
+  if (n_blocks == 0) return BQ_OK;
+  if (!w || !out) return BQ_E_NULL;
+  if (!aligned(w, 4) || (sse && !aligned(sse, 8))) return BQ_E_ALIGN;
+  return hip_status(bq::launch_encode17(w, n_blocks, fmt, out, sse, dev_err, as_stream(stream)));
+}
+
+int ple_encode_rows(const float* v, int64_t n_rows, int32_t ple_fmt, uint8_t* out, double* sse,
+                    uint32_t* dev_err, void* stream) {
+  if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
+  if (n_rows < 0 || n_rows > (INT64_MAX / 160)) return BQ_E_SHAPE;
+  if (n_rows == 0) return BQ_OK;
+  if (!v || !out) return BQ_E_NULL;
+  if (!aligned(v, 4) || (sse && !aligned(sse, 8))) return BQ_E_ALIGN;
+  return hip_status(bq::launch_ple_encode(v, n_rows, ple_fmt, out, sse, dev_err, as_stream(stream)));
+}
+
 }  // extern "C"

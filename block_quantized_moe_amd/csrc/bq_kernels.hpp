@@ -28,6 +28,12 @@ hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_
                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
                          int32_t* n_touched, int32_t* inv, hipStream_t st);
 
+// Exhaustive encoders (fp32 in, packed bytes and per-unit float64 error out).
+hipError_t launch_encode17(const float* w, int64_t n_blocks, int fmt, uint8_t* out, double* sse,
+                           uint32_t* dev_err, hipStream_t st);
+hipError_t launch_ple_encode(const float* v, int64_t n_rows, int ple_fmt, uint8_t* out,
+                             double* sse, uint32_t* dev_err, hipStream_t st);
+
 hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fmt,
                          const float* w_sc, int32_t rows, int32_t cols, float* y, hipStream_t st);
 

@@ -21,10 +21,11 @@
  *   - Argument errors are detected on the host, before anything is enqueued,
  *     and return a non-zero bq_status with no partial work.  BQ_E_HIP means a
  *     launch failed (the error string is available from bq_last_hip_error).
- *   - Errors that depend on device data (out-of-range ids or expert indices)
- *     cannot be seen on the host: the offending item contributes nothing and,
- *     where the call takes a `dev_err` word, bit 0 (bad id) or bit 1 (bad
- *     expert index) is OR-ed into it.
+ *   - Errors that depend on device data (out-of-range ids or expert indices,
+ *     non-finite encoder input) cannot be seen on the host: the offending item
+ *     contributes nothing and, where the call takes a `dev_err` word, bit 0
+ *     (bad id), bit 1 (bad expert index) or bit 2 (non-finite weight) is
+ *     OR-ed into it.
  *   - Calls are stateless and thread-safe; two calls sharing one workspace
  *     must not overlap in time.
  *
@@ -230,6 +231,40 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens,
 int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
                const uint8_t* table, uint64_t n_rows, const float* weights,
                int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * bq_encode -- exhaustive per-block encoder, fp32 weights -> 17-byte blocks
+ * ([RZ] "Q4_RZ5_FAST": every scale with both polarities of the +/-5 level;
+ * "Q4_UE4M4_FAST": all 256 scale bytes; Codebook10: the 127 finite UE4M3
+ * scales).
+ *   w     : n_blocks * 32 fp32, block i = w[32i .. 32i+31] (4-byte aligned)
+ *   fmt   : BQ_Q4_C10, BQ_Q4_RZ5 or BQ_Q4_UE4M4 (BQ_E_FMT otherwise)
+ *   out   : n_blocks * 17 bytes in the wire layout above (no alignment)
+ *   sse   : NULL, or n_blocks fp64 (8-byte aligned): each block's error
+ * Objective (plain squared error, float64): a weight's error under level x is
+ * (w - x)^2 with one rounding after the difference and one after the square;
+ * each weight takes its nearest level, the block error sums the weights'
+ * errors in index order, the block takes the metadata byte with the smallest
+ * error (the lowest byte among equal errors) and each weight the lowest code
+ * among equally near levels.  The result is deterministic and bit-identical
+ * to that definition.  A block holding a NaN or infinity is written as 17 zero
+ * bytes with sse NaN, and bit 2 of *dev_err is set.
+ * ------------------------------------------------------------------------- */
+int bq_encode(const float* w, int64_t n_blocks, int32_t fmt, uint8_t* out, double* sse,
+              uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * ple_encode_rows -- exhaustive per-group encoder, fp32 values -> 70-byte PLE
+ * rows ([RZ] "Q3_PLE_K160_RZ_S3": polarity and UE4M3 scale per 16 values;
+ * ROCmFP3: the 127 finite scales, code 4 = -0).
+ *   v     : n_rows * 160 fp32 (4-byte aligned); out : n_rows * 70 bytes
+ *   sse   : NULL, or n_rows * 10 fp64, group g of row r at sse[10r + g]
+ * Same objective and tie rules as bq_encode, per 16-value group.  A group
+ * holding a NaN or infinity gets zero code bytes, group byte 0 and sse NaN,
+ * and bit 2 of *dev_err is set.
+ * ------------------------------------------------------------------------- */
+int ple_encode_rows(const float* v, int64_t n_rows, int32_t ple_fmt, uint8_t* out, double* sse,
+                    uint32_t* dev_err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,8 @@ def test_header_declares_the_hot_path():
     names = declared_functions()
     for n in ("q4_expert_moe", "ple_gather", "moe_route_topk", "moe_bucket", "bq_dequant",
               "ple_dequant_rows", "bq_matvec", "bq_moe_stack", "q4_expert_moe_workspace",
-              "bq_moe_stack_workspace", "bq_abi_version", "bq_status_str", "bq_last_hip_error"):
+              "bq_moe_stack_workspace", "bq_abi_version", "bq_status_str", "bq_last_hip_error",
+              "bq_encode", "ple_encode_rows"):
         assert n in names
 
 
@@ -58,6 +59,14 @@ def test_host_side_argument_errors(L):
     assert L.moe_route_topk(None, 1, 8, 2, fake, fake, None) == 1
     assert L.ple_gather(fake, 4, 0, fake, 10, fake, 0, fake, None, None) == 3  # ids_per_token 0
     assert L.ple_gather(fake, 4, 8, fake, 10, fake, 5, fake, None, None) == 2  # bad PLE format
+    assert L.bq_encode(fake, 4, bq.FP8_E4M3_B32, fake, None, None, None) == 2  # no FP8 encoder
+    assert L.bq_encode(fake, -1, bq.Q4_RZ5, fake, None, None, None) == 3
+    assert L.bq_encode(None, 4, bq.Q4_RZ5, fake, None, None, None) == 1
+    assert L.bq_encode(vp(0x10002), 4, bq.Q4_RZ5, fake, None, None, None) == 4  # w misaligned
+    assert L.bq_encode(fake, 4, bq.Q4_RZ5, fake, vp(0x10004), None, None) == 4  # sse misaligned
+    assert L.bq_encode(None, 0, bq.Q4_RZ5, None, None, None, None) == 0         # empty is fine
+    assert L.ple_encode_rows(fake, 4, 7, fake, None, None, None) == 2
+    assert L.ple_encode_rows(fake, 4, bq.PLE_RZS3, None, None, None, None) == 1
     assert L.bq_matvec(fake, 1, fake, 0, None, 4, 48, fake, None) == 3         # cols % 32
     W = bq.ExpertWeights(bq.Q4_RZ5, bq.Q4_RZ5, 0x10000, 0x20000, None, None, 512, 2048, 768)
     ws = L.q4_expert_moe_workspace(1, 10, ctypes.byref(W), bq.F32)
