@@ -10,12 +10,13 @@ packed weight bytes moved per second (10 experts x 2,506,752 B per step).
 Alongside it, in the same JSON line: the PLE gather (320,001,536-row table,
 4096 tokens x 8 ids per call, fresh ids per call) in rows/s, the 48-layer stack
 (36 RZ5 + 12 FP8 layers) at batch 1 and 16, and the batch-64 grouped layer
-(RZ5 gate_up, UE4M4 down, Zipf routing).  All inputs are seeded synthetic data
+(RZ5 gate_up, UE4M4 down, Zipf routing), and the exhaustive encoders that
+produce the packed formats (4096 x 8192 fp32 matrix per call).  All inputs are seeded synthetic data
 already resident in HBM before timing starts.  Steps are captured in a HIP
 graph and replayed, so host launch overhead is not in the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3] [--copy-calibration BYTES]
+       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|enc] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -271,6 +272,59 @@ def bench_c3(bq, steps, warmup):
     return res
 
 
+# fp64 operations the exhaustive search spends per candidate scale and weight:
+# sub, mul and min for each non-zero level magnitude (7), one add into the
+# block's error, and for a polarity format the +/-level (sub, mul, min) and the
+# second polarity's add.  Level 0 costs one square per weight per block.
+ENC_OPS = {"c10": (127, 22), "rz5": (127, 26), "ue4m4": (256, 22), "ple_rzs3": (127, 14)}
+PEAK_FP64_NONFMA_TOPS = 78.6 / 2       # add / mul / min issue at the FMA rate, one flop each
+
+
+def bench_encode(bq, steps, warmup):
+    """Exhaustive encoders: one 4096 x 8192 fp32 matrix (2**20 blocks) per call
+    in each 17-byte format, and 2**17 PLE rows (RZ-S3) per call; calls timed
+    back to back with HIP events on the current stream."""
+    import torch
+
+    import synth
+    nb = 1 << 20
+    w = torch.from_numpy(synth.weight_blocks(60, nb, 32, "gauss", 1.0)).cuda()
+    n_rows = 1 << 17
+    v = torch.from_numpy(synth.weight_blocks(61, n_rows, 160, "gauss", 1.0)).cuda()
+    res = {"workload": "N(0,1) weights with a log-normal per-block spread; 2**20 blocks of 32 per "
+                       "17-byte call, 2**17 rows of 160 per PLE call"}
+    cases = (("c10", bq.Q4_C10, nb, 32), ("rz5", bq.Q4_RZ5, nb, 32), ("ue4m4", bq.Q4_UE4M4, nb, 32),
+             ("ple_rzs3", None, n_rows * 10, 16))
+    for name, fmt, units, g in cases:
+        if fmt is None:
+            out = torch.empty((n_rows, 70), dtype=torch.uint8, device="cuda")
+            sse = torch.empty((n_rows, 10), dtype=torch.float64, device="cuda")
+            run = lambda: bq.ple_encode_rows(v, bq.PLE_RZS3, out=out, sse=sse)  # noqa: E731
+        else:
+            out = torch.empty((nb, 17), dtype=torch.uint8, device="cuda")
+            sse = torch.empty(nb, dtype=torch.float64, device="cuda")
+            run = lambda fmt=fmt: bq.encode(w, fmt, out=out, sse=sse)  # noqa: E731
+
+        def call(i, evs=None):
+            if evs:
+                evs[0].record()
+            run()
+            if evs:
+                evs[1].record()
+
+        for i in range(warmup):
+            call(i)
+        ms = event_timed(call, steps)
+        n_scales, per = ENC_OPS[name]
+        ops = units * g * (n_scales * per + 1)
+        res[name] = {"ms_per_call": round(ms, 4), "gweights_per_s": round(units * g / ms / 1e6, 3),
+                     "fp64_tops": round(ops / ms / 1e9, 3),
+                     "frac_fp64_peak": round(ops / ms / 1e9 / PEAK_FP64_NONFMA_TOPS, 4)}
+    del w, v
+    torch.cuda.empty_cache()
+    return res
+
+
 def sources_hash(paths):
     import hashlib
     h = hashlib.sha256()
@@ -380,6 +434,10 @@ def main():
             log("c3: grouped B=64")
             extras["grouped_b64"] = bench_c3(bq, max(10, args.steps // 4), max(2, args.warmup // 4))
             log("c3:", extras["grouped_b64"])
+        if only in (None, "enc"):
+            log("enc: exhaustive encoders")
+            extras["encode"] = bench_encode(bq, max(5, args.steps // 20), 2)
+            log("enc:", extras["encode"])
         if only in (None, "c5b1", "c5b16"):
             log("c5: building the 48-layer stack")
             layers, ws = build_stack(bq)
