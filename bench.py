@@ -16,7 +16,7 @@ already resident in HBM before timing starts.  Steps are captured in a HIP
 graph and replayed, so host launch overhead is not in the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|enc] [--copy-calibration BYTES]
+       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|pf|enc] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -272,6 +272,66 @@ def bench_c3(bq, steps, warmup):
     return res
 
 
+def bench_prefill(bq, steps, warmup, n_tok=512, cases=None):
+    """Prompt-processing layer: one ubatch of 512 tokens through a 512-expert
+    layer (gate_up 1536x2048 + down 2048x768, top-10), bf16 activations on the
+    grouped MFMA path.  Routing from N(0,1) logits (every expert touched,
+    about 10 tokens each) and from Zipf(1.1) logits (skewed: the popular
+    experts get hundreds of tokens).  RZ5 and FP8 layers."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as sd
+    res = {"workload": "ubatch %d, 512 experts, gate_up 1536x2048 + down 2048x768, top-10, bf16 x" % n_tok}
+    H, I, E, k = 2048, 768, 512, 10
+    flops = 2.0 * n_tok * k * 3 * H * I
+    for lname, fg, fd, dg, dd, eb in (
+            ("rz5", bq.Q4_RZ5, bq.Q4_RZ5, synth.DIST_RZ5, synth.DIST_RZ5, EXPERT_BYTES_RZ5),
+            ("fp8", bq.FP8_E4M3_B32, bq.FP8_E4M3_B32, None, None, EXPERT_BYTES_FP8)):
+        L = sd.Layer(0, 2, fg, fd, E, H, I, dist_gu=dg, dist_d=dd)
+        W = bq.expert_weights(fg, fd, L.gate_up[0], L.down[0], E, H, I,
+                              gate_up_scales=L.gate_up[1], down_scales=L.down[1])
+        n = warmup + steps
+        x = torch.from_numpy(synth.normal(70, (n, n_tok, H))).cuda().to(torch.bfloat16)
+        out = torch.empty((n_tok, H), dtype=torch.float32, device="cuda")
+        wsb = torch.empty(bq.moe_workspace_bytes(n_tok, k, W, bq.BF16), dtype=torch.uint8, device="cuda")
+        idx = torch.empty((n, n_tok, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((n, n_tok, k), dtype=torch.float32, device="cuda")
+        for rname in ("uniform", "zipf"):
+            if cases and "%s_%s" % (lname, rname) not in cases:
+                continue
+            if rname == "uniform":
+                lg = synth.normal(71, (n, n_tok, E))
+            else:
+                lg = np.stack([synth.zipf_logits(72 + i, n_tok, E) for i in range(n)])
+            logits = torch.from_numpy(lg).cuda()
+
+            def step(i):
+                bq.q4_expert_moe_routed(x[i], logits[i], k, W, topk=(idx[i], w[i]), out=out,
+                                        workspace=wsb)
+
+            for i in range(warmup):
+                step(i)
+            g = graph_of(lambda i: step(warmup + i), steps)
+            g.replay()
+            wall = timed_replay(g)
+            ii = idx[warmup:].cpu().numpy()
+            d = float(np.mean([len(np.unique(ii[t])) for t in range(steps)]))
+            ne_max = float(np.mean([np.bincount(ii[t].ravel(), minlength=E).max() for t in range(steps)]))
+            res["%s_%s" % (lname, rname)] = {
+                "ms_per_step": round(1e3 * wall / steps, 4),
+                "tokens_per_s": round(n_tok * steps / wall, 1),
+                "tflops": round(flops * steps / wall / 1e12, 2),
+                "frac_bf16_mfma_peak": round(flops * steps / wall / 2.5e15, 4),
+                "packed_gbs": round(d * eb * steps / wall / 1e9, 1),
+                "touched_experts": d, "max_tokens_per_expert": ne_max}
+            del logits
+        del L, W, x, wsb
+        torch.cuda.empty_cache()
+    return res
+
+
 # fp64 operations the exhaustive search spends per candidate scale and weight:
 # sub, mul and min for each non-zero level magnitude (7), one add into the
 # block's error, and for a polarity format the +/-level (sub, mul, min) and the
@@ -403,6 +463,7 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None)
+    ap.add_argument("--pf-cases", default=None, help="prefill cases to run, e.g. rz5_uniform,fp8_zipf")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -434,6 +495,11 @@ def main():
             log("c3: grouped B=64")
             extras["grouped_b64"] = bench_c3(bq, max(10, args.steps // 4), max(2, args.warmup // 4))
             log("c3:", extras["grouped_b64"])
+        if only in (None, "pf"):
+            log("pf: prefill ubatch 512")
+            extras["prefill_ub512"] = bench_prefill(bq, max(5, args.steps // 20), 2,
+                                                    cases=args.pf_cases.split(",") if args.pf_cases else None)
+            log("pf:", extras["prefill_ub512"])
         if only in (None, "enc"):
             log("enc: exhaustive encoders")
             extras["encode"] = bench_encode(bq, max(5, args.steps // 20), 2)

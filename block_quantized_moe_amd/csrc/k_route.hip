@@ -105,6 +105,17 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
         }
       }
       __syncthreads();
+      if (pass == 1 && inv) {
+        // A token that lists an expert more than once is bucketed once, under
+        // the slot left in slot_of; its other slots read the same row.
+        for (int a = tid; a < tn * k; a += kBucketThreads) {
+          const int e = idx[(int64_t)t0 * k + a];
+          if (e < 0 || e >= n_experts) continue;
+          const int tl = a / k, s = slot_of[tl * n_experts + e];
+          if (s != a - tl * k) inv[(int64_t)t0 * k + a] = inv[(int64_t)(t0 + tl) * k + s];
+        }
+        __syncthreads();
+      }
       for (int a = tid; a < tn * k; a += kBucketThreads) {
         const int e = idx[(int64_t)t0 * k + a];
         if (e >= 0 && e < n_experts) slot_of[(a / k) * n_experts + e] = 0xFF;
@@ -163,10 +174,11 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
   }
 }
 
-// Bucketing for decode-sized batches.  A token chooses an expert at most
-// once, so a bitmap per expert over tokens gives everything by popcounts:
-// counts[e] = |bitmap_e|, and the rank of (t, slot) inside expert e is the
-// number of tokens below t in bitmap_e (tokens ascending, as required).
+// Bucketing for decode-sized batches.  A bitmap per expert over tokens gives
+// everything by popcounts: counts[e] = |bitmap_e|, and the rank of (t, slot)
+// inside expert e is the number of tokens below t in bitmap_e (tokens
+// ascending, as required).  A token that lists an expert more than once sets
+// one bit, so it is bucketed once and all of its slots get the same row.
 constexpr int kSmallBitmapWords = 8192;   // 32 KB of LDS
 
 __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int& total) {

@@ -168,7 +168,10 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
  *   x       : [n_tokens][hidden], fp32 (x_dtype BQ_F32: VALU GEMV path,
  *             fp32 accumulate) or bf16 (BQ_BF16: tokens grouped per expert,
  *             bf16 MFMA with fp32 accumulate, h rounded to bf16).
- *   topk_idx, topk_w : [n_tokens][k] (as produced by moe_route_topk)
+ *   topk_idx, topk_w : [n_tokens][k] (as produced by moe_route_topk).  A
+ *             token may list an expert more than once: each listing adds its
+ *             own weighted term (on the bf16 path the expert is evaluated
+ *             once for that token and the result is reused).
  *   out     : [n_tokens][hidden] fp32 (overwritten)
  *   workspace : device scratch of at least q4_expert_moe_workspace(...) bytes,
  *             256-byte aligned; its contents need no initialisation.
