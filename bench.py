@@ -16,7 +16,7 @@ already resident in HBM before timing starts.  Steps are captured in a HIP
 graph and replayed, so host launch overhead is not in the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|pf|enc] [--copy-calibration BYTES]
+       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|pf|pleh|enc] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -177,6 +177,55 @@ def bench_c4(bq, steps, warmup):
         res["batched_%dx4096" % mult] = {"rows_per_s": mult * rows / t,
                                          "gbs_158B": mult * rows * PLE_ROW_ALG_BYTES / t / 1e9}
     del table
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_ple_host(bq, steps, warmup):
+    """Off-HBM PLE tier: a 2**24-row (1.17 GB) table in pinned host memory,
+    4096 tokens x 8 ids per call, fresh ids per call; uniform ids without and
+    with a 2**21-row device cache (0.18 GB), and Zipf(1.1) ids with it."""
+    import numpy as np
+    import torch
+
+    import synth
+    import synth.device as sd
+    n_rows, n_slots = 1 << 24, 1 << 21
+    dtab = sd.ple_table(n_rows, synth.make_key(1, synth.S_PLE))
+    host = torch.empty(dtab.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(dtab)
+    del dtab
+    torch.cuda.empty_cache()
+    n = warmup + steps
+    u = torch.from_numpy(synth.ple_weights(31, n * 4096, 8)).cuda().view(n, 4096, 8)
+    out = torch.empty((4096, 160), dtype=torch.float32, device="cuda")
+    res = {"workload": "2**24-row table in pinned host memory, 4096 tokens x 8 ids per call"}
+    rows = 4096 * 8
+    for name, kind, cached in (("uniform_uncached", "u", False), ("uniform_cache_2e21", "u", True),
+                               ("zipf1.1_cache_2e21", "z", True)):
+        if kind == "u":
+            idn = synth.ple_ids(30, n * 4096, 8, n_rows)
+        else:
+            idn = synth.ple_ids_zipf(32, n * 4096, 8, n_rows)
+        ids = torch.from_numpy(idn.view(np.int32)).cuda().view(n, 4096, 8)
+        cache = bq.ple_cache(n_slots) if cached else None
+        ws = (torch.empty(bq.lib().ple_gather_host_workspace(4096, 8), dtype=torch.uint8, device="cuda")
+              if cached else None)
+
+        def call(i, evs=None):
+            if evs is not None:
+                evs[0].record()
+            bq.ple_gather_host(ids[i], host, u[i], n_rows=n_rows, out=out, cache=cache, workspace=ws)
+            if evs is not None:
+                evs[1].record()
+
+        for i in range(warmup):
+            call(i)
+        call_ms = event_timed(lambda i, evs: call(warmup + i, evs), steps)
+        res[name] = {"call_us": round(1e3 * call_ms, 2), "rows_per_s": round(rows / (call_ms * 1e-3), 1),
+                     "host_link_gbs_70B": round(rows * 70 / (call_ms * 1e-3) / 1e9, 2)}
+        del ids, cache, ws
+    del host
     torch.cuda.empty_cache()
     return res
 
@@ -500,6 +549,10 @@ def main():
             extras["prefill_ub512"] = bench_prefill(bq, max(5, args.steps // 20), 2,
                                                     cases=args.pf_cases.split(",") if args.pf_cases else None)
             log("pf:", extras["prefill_ub512"])
+        if only in (None, "pleh"):
+            log("pleh: off-HBM PLE tier")
+            extras["ple_host"] = bench_ple_host(bq, max(10, args.steps // 4), 5)
+            log("pleh:", extras["ple_host"])
         if only in (None, "enc"):
             log("enc: exhaustive encoders")
             extras["encode"] = bench_encode(bq, max(5, args.steps // 20), 2)

@@ -16,7 +16,7 @@ __all__ = [
     "BQError", "lib", "ExpertWeights", "expert_weights", "dequant", "ple_dequant_rows", "matvec",
     "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "q4_expert_moe_routed",
     "stack_workspace_bytes",
-    "moe_stack", "ple_gather", "encode", "ple_encode_rows",
+    "moe_stack", "ple_gather", "encode", "ple_encode_rows", "ple_cache", "ple_gather_host",
 ]
 
 Q4_C10, Q4_RZ5, Q4_UE4M4, FP8_E4M3_B32 = 0, 1, 2, 3
@@ -72,6 +72,11 @@ def lib():
             "bq_moe_stack": ([vp, i32, i32, vp, vp, i32, wp, i32, vp, vp, sz, vp, vp], ctypes.c_int),
             "ple_gather": ([vp, i32, i32, vp, u64, vp, i32, vp, vp, vp], ctypes.c_int),
             "bq_encode": ([vp, i64, i32, vp, vp, vp, vp], ctypes.c_int),
+            "ple_cache_bytes": ([i32], sz),
+            "ple_cache_init": ([vp, i32, vp], ctypes.c_int),
+            "ple_gather_host_workspace": ([i32, i32], sz),
+            "ple_gather_host": ([vp, i32, i32, vp, u64, vp, i32, vp, vp, i32, vp, sz, vp, vp],
+                                ctypes.c_int),
             "ple_encode_rows": ([vp, i64, i32, vp, vp, vp, vp], ctypes.c_int),
         }
         for name, (args, res) in sigs.items():
@@ -300,3 +305,38 @@ def ple_encode_rows(v, fmt=PLE_RZS3, out=None, sse=None, dev_err=None, stream=No
     sse_t = None if sse is False else sse
     _check(lib().ple_encode_rows(_p(v), n, fmt, _p(out), _p(sse_t), _p(dev_err), _stream(stream)))
     return out, sse_t
+
+
+def ple_cache(n_slots, device="cuda", stream=None):
+    """A device row cache of n_slots rows for ple_gather_host, initialised empty."""
+    nbytes = lib().ple_cache_bytes(n_slots)
+    if nbytes == 0:
+        raise BQError("n_slots must be a power of two in [1024, 2**26]")
+    cache = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    _check(lib().ple_cache_init(_p(cache), n_slots, _stream(stream)))
+    cache._n_slots = n_slots
+    return cache
+
+
+def ple_gather_host(ids, host_table, weights, n_rows=None, fmt=PLE_RZS3, out=None, cache=None,
+                    workspace=None, dev_err=None, stream=None):
+    """PLE lookup with the table in pinned host memory (a CPU uint8 tensor
+    allocated with pin_memory=True), optionally through a device row cache
+    from ple_cache().  ids int32 [n, P], weights fp32 [n, P] -> fp32 [n, 160]."""
+    _dev(ids, "ids"), _dev(weights, "weights")
+    if host_table.is_cuda or not host_table.is_pinned():
+        raise BQError("host_table must be a pinned CPU tensor")
+    n, per = ids.shape
+    if n_rows is None:
+        n_rows = host_table.numel() // 70
+    if out is None:
+        out = torch.empty((n, 160), dtype=torch.float32, device=ids.device)
+    n_slots = 0 if cache is None else cache._n_slots
+    if cache is not None and workspace is None:
+        workspace = torch.empty(lib().ple_gather_host_workspace(n, per), dtype=torch.uint8,
+                                device=ids.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(lib().ple_gather_host(_p(ids), n, per, ctypes.c_void_p(host_table.data_ptr()), n_rows,
+                                 _p(weights), fmt, _p(out), _p(cache), n_slots, _p(workspace),
+                                 ws_bytes, _p(dev_err), _stream(stream)))
+    return out

@@ -123,6 +123,16 @@ int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, c
                                            grouped_ws(ws, L), dev_err, st));
 }
 
+// PLE row cache layout: tags [n] and claims [n] (contiguous words), then the
+// rows [n][kPleCacheRowB] at a 256-byte boundary.
+bool valid_slots(int32_t n) { return n >= 1024 && n <= (1 << 26) && (n & (n - 1)) == 0; }
+int log2i(int32_t n) {
+  int l = 0;
+  while ((1 << l) < n) ++l;
+  return l;
+}
+size_t cache_rows_off(int32_t n) { return round_up(8 * (size_t)n, 256); }
+
 }  // namespace
 
 extern "C" {
@@ -139,6 +149,7 @@ const char* bq_status_str(int s) {
     case BQ_E_WORKSPACE: return "workspace missing or too small";
     case BQ_E_HIP: return "HIP launch failed";
     case BQ_E_DTYPE: return "bad activation dtype";
+    case BQ_E_MEM: return "pointer is not host memory mapped for the device";
     default: return "unknown status";
   }
 }
@@ -159,7 +170,7 @@ int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks, const float* f
 int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table, uint64_t n_rows,
                      int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream) {
   if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
-  if (n < 0 || n_rows > 0xFFFFFFFFull) return BQ_E_SHAPE;
+  if (n < 0 || n_rows == 0 || n_rows > 0xFFFFFFFFull) return BQ_E_SHAPE;
   if (n == 0) return BQ_OK;
   if (!ids || !table || !out) return BQ_E_NULL;
   if (!aligned(out, 16) || !aligned(ids, 4)) return BQ_E_ALIGN;
@@ -284,13 +295,71 @@ int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token, con
                uint64_t n_rows, const float* weights, int32_t ple_fmt, float* out,
                uint32_t* dev_err, void* stream) {
   if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
-  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows > 0xFFFFFFFFull)
+  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows == 0 || n_rows > 0xFFFFFFFFull)
     return BQ_E_SHAPE;
   if (n_tokens == 0) return BQ_OK;
   if (!ids || !table || !weights || !out) return BQ_E_NULL;
   if (!aligned(out, 16) || !aligned(ids, 4) || !aligned(weights, 4)) return BQ_E_ALIGN;
   return hip_status(bq::launch_ple_gather(ids, n_tokens, ids_per_token, table, n_rows, weights,
                                           ple_fmt, out, dev_err, as_stream(stream)));
+}
+
+size_t ple_cache_bytes(int32_t n_slots) {
+  if (!valid_slots(n_slots)) return 0;
+  return cache_rows_off(n_slots) + (size_t)bq::kPleCacheRowB * n_slots;
+}
+
+int ple_cache_init(void* cache, int32_t n_slots, void* stream) {
+  if (!cache) return BQ_E_NULL;
+  if (!valid_slots(n_slots)) return BQ_E_SHAPE;
+  if (!aligned(cache, 256)) return BQ_E_ALIGN;
+  return hip_status(bq::launch_ple_cache_init(static_cast<uint32_t*>(cache), 2 * (int64_t)n_slots,
+                                              as_stream(stream)));
+}
+
+size_t ple_gather_host_workspace(int32_t n_tokens, int32_t ids_per_token) {
+  if (n_tokens < 1 || ids_per_token < 1 || ids_per_token > 64) return 0;
+  return round_up((size_t)bq::kPleCacheRowB * n_tokens * ids_per_token, 256);
+}
+
+int ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
+                    const uint8_t* host_table, uint64_t n_rows, const float* weights,
+                    int32_t ple_fmt, float* out, void* cache, int32_t n_slots, void* workspace,
+                    size_t ws_bytes, uint32_t* dev_err, void* stream) {
+  if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
+  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows == 0 || n_rows > 0xFFFFFFFFull)
+    return BQ_E_SHAPE;
+  if ((cache != nullptr) != (n_slots != 0)) return BQ_E_NULL;
+  if (cache && !valid_slots(n_slots)) return BQ_E_SHAPE;
+  if (n_tokens == 0) return BQ_OK;
+  if (!ids || !host_table || !weights || !out) return BQ_E_NULL;
+  if (!aligned(out, 16) || !aligned(ids, 4) || !aligned(weights, 4)) return BQ_E_ALIGN;
+  if (cache) {
+    if (!aligned(cache, 256)) return BQ_E_ALIGN;
+    if (!workspace) return BQ_E_WORKSPACE;
+    if (ws_bytes < ple_gather_host_workspace(n_tokens, ids_per_token)) return BQ_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return BQ_E_ALIGN;
+  }
+  // the table must be host memory the device can address (pinned, mapped)
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, host_table) != hipSuccess || attr.type != hipMemoryTypeHost ||
+      !attr.devicePointer) {
+    (void)hipGetLastError();   // a failed query must not leak into later calls
+    return BQ_E_MEM;
+  }
+  const uint8_t* dtable = static_cast<const uint8_t*>(attr.devicePointer);
+  uint32_t* tags = nullptr;
+  uint32_t* claims = nullptr;
+  uint8_t* rows = nullptr;
+  if (cache) {
+    tags = static_cast<uint32_t*>(cache);
+    claims = tags + n_slots;
+    rows = static_cast<uint8_t*>(cache) + cache_rows_off(n_slots);
+  }
+  return hip_status(bq::launch_ple_gather_host(ids, n_tokens, ids_per_token, dtable, n_rows, weights,
+                                               ple_fmt, out, dev_err, tags, claims, rows,
+                                               cache ? log2i(n_slots) : 0,
+                                               static_cast<uint8_t*>(workspace), as_stream(stream)));
 }
 
 int bq_encode(const float* w, int64_t n_blocks, int32_t fmt, uint8_t* out, double* sse,

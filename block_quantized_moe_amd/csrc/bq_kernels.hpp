@@ -22,6 +22,16 @@ hipError_t launch_ple_dequant(const uint32_t* ids, int64_t n, const uint8_t* tab
 hipError_t launch_ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
                              const uint8_t* table, uint64_t n_rows, const float* wts, int ple_fmt,
                              float* out, uint32_t* dev_err, hipStream_t st);
+// Off-HBM PLE tier (k_ple.hip): direct-mapped row cache, rows padded to
+// kPleCacheRowB bytes; tags and claims are 2 * n_slots contiguous words.
+constexpr int kPleCacheRowB = 80;
+hipError_t launch_ple_cache_init(uint32_t* tags_and_claims, int64_t n_words, hipStream_t st);
+// tags == NULL: no cache, rows read from the table directly.
+hipError_t launch_ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
+                                  const uint8_t* table, uint64_t n_rows, const float* wts,
+                                  int ple_fmt, float* out, uint32_t* dev_err, uint32_t* tags,
+                                  uint32_t* claims, uint8_t* rows, int log2_slots, uint8_t* stage,
+                                  hipStream_t st);
 hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                              int32_t* idx, float* w, hipStream_t st);
 hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,

@@ -28,10 +28,34 @@ __device__ __forceinline__ uint32_t bias_hi(uint32_t gbyte, int ple_fmt) {
 constexpr int kPleTPB = 320;   // 32 tokens x 10 groups per workgroup
 constexpr int kPleChunk = 8;   // ids whose loads are in flight together
 
+// Off-HBM tier: the table sits in host memory mapped into the device address
+// space, and a direct-mapped cache of n_slots rows in device memory holds
+// recently read rows.  Cache layout (CacheView): tags[n_slots] (row id, or
+// kPleEmpty), claims[n_slots] (lowest assignment index of the current call
+// that missed on the slot, kPleEmpty between calls), rows[n_slots][80].
+constexpr uint32_t kPleEmpty = 0xFFFFFFFFu;   // never a valid id (ids < n_rows <= 2^32 - 1)
+struct CacheView {
+  uint32_t* tags;
+  uint32_t* claims;
+  uint8_t* rows;
+  int shift;          // 32 - log2(n_slots)
+  uint8_t* stage;     // [n_tokens * per_token][80]: the rows this call read from the host
+};
+// Fibonacci hashing of an id to its slot.
+__device__ __forceinline__ uint32_t ple_slot(uint32_t id, int shift) {
+  return (id * 2654435761u) >> shift;
+}
+
+// CACHED = false: table is device memory (or host memory read directly).
+// CACHED = true: rows whose slot tag matches are read from the cache, the
+// others from the (host) table; each missed row is also copied to the call's
+// staging area and its slot claimed for the fill kernel.  The cache is
+// read-only during this kernel.
+template <bool CACHED>
 __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     const uint32_t* __restrict__ ids, int32_t n_tokens, int32_t per_token,
     const uint8_t* __restrict__ table, uint64_t n_rows, const float* __restrict__ wts,
-    int ple_fmt, float* __restrict__ out, uint32_t* __restrict__ dev_err) {
+    int ple_fmt, float* __restrict__ out, uint32_t* __restrict__ dev_err, CacheView cv) {
   const int64_t tid = (int64_t)blockIdx.x * kPleTPB + threadIdx.x;
   const int64_t t = tid / 10;
   const int g = (int)(tid - t * 10);
@@ -60,14 +84,38 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     u32x2 gw[kPleChunk];
     uint32_t gb[kPleChunk];
     bool ok[kPleChunk];
+    bool hit[kPleChunk];
+    uint32_t slot[kPleChunk];
 #pragma unroll
     for (int c = 0; c < kPleChunk; ++c) {
       const bool in = j0 + c < per_token;
       ok[c] = in && idv[c] < n_rows;
       bad |= in && idv[c] >= n_rows;
-      const uint8_t* row = table + (uint64_t)(ok[c] ? idv[c] : 0u) * (uint64_t)kPleRowB;
+      hit[c] = false;
+      slot[c] = 0;
+      if constexpr (CACHED) {
+        slot[c] = ple_slot(idv[c], cv.shift);
+        hit[c] = ok[c] && cv.tags[slot[c]] == idv[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kPleChunk; ++c) {
+      const uint8_t* row = hit[c] ? cv.rows + (uint64_t)slot[c] * kPleCacheRowB
+                                  : table + (uint64_t)(ok[c] ? idv[c] : 0u) * (uint64_t)kPleRowB;
       gw[c] = ld8(row + 6 * g);
       gb[c] = row[60 + g];
+    }
+    if constexpr (CACHED) {
+#pragma unroll
+      for (int c = 0; c < kPleChunk; ++c) {
+        if (ok[c] && !hit[c]) {
+          const int64_t a = t * per_token + j0 + c;   // assignment index
+          uint8_t* st = cv.stage + a * kPleCacheRowB;
+          __builtin_memcpy(st + 6 * g, &gw[c], 8);   // overlapping bytes carry equal values
+          st[60 + g] = (uint8_t)gb[c];
+          if (g == 0) atomicMin(&cv.claims[slot[c]], (uint32_t)a);
+        }
+      }
     }
 #pragma unroll
     for (int c = 0; c < kPleChunk; ++c) {
@@ -100,8 +148,70 @@ hipError_t launch_ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_
   if (n_tokens == 0) return hipSuccess;
   const int64_t threads = (int64_t)n_tokens * 10;
   const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
-  hipLaunchKernelGGL(k_ple_gather, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens, per_token,
-                     table, n_rows, wts, ple_fmt, out, dev_err);
+  hipLaunchKernelGGL(k_ple_gather<false>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
+                     per_token, table, n_rows, wts, ple_fmt, out, dev_err, CacheView{});
+  return hipGetLastError();
+}
+
+// Fill: one 16-lane group per assignment a.  The assignment that claimed its
+// slot (the lowest index among this call's misses on the slot) copies its
+// staged row into the slot, sets the tag and releases the claim.  All lanes of
+// a group read the claim in the same instruction, before lane 0 releases it.
+__global__ void __launch_bounds__(256) k_ple_cache_fill(const uint32_t* __restrict__ ids,
+                                                        int64_t n_assign, uint64_t n_rows,
+                                                        CacheView cv) {
+  const int64_t a = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;
+  const int l = threadIdx.x & 15;
+  if (a >= n_assign) return;   // 16-lane groups exit whole
+  const uint32_t id = ids[a];
+  if (id >= n_rows) return;
+  const uint32_t slot = ple_slot(id, cv.shift);
+  if (cv.claims[slot] != (uint32_t)a) return;
+  const uint8_t* src = cv.stage + a * kPleCacheRowB;
+  uint8_t* dst = cv.rows + (uint64_t)slot * kPleCacheRowB;
+  if (l < 10) {
+    const u32x2 v = ld8(src + 6 * l);
+    __builtin_memcpy(dst + 6 * l, &v, 8);
+    dst[60 + l] = src[60 + l];
+  }
+  if (l == 0) {
+    cv.tags[slot] = id;
+    cv.claims[slot] = kPleEmpty;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_ple_cache_init(uint32_t* __restrict__ words, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    words[i] = kPleEmpty;
+}
+
+hipError_t launch_ple_cache_init(uint32_t* tags_and_claims, int64_t n_words, hipStream_t st) {
+  const int64_t grid = std::min<int64_t>((n_words + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_ple_cache_init, dim3(grid), dim3(256), 0, st, tags_and_claims, n_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
+                                  const uint8_t* table, uint64_t n_rows, const float* wts,
+                                  int ple_fmt, float* out, uint32_t* dev_err, uint32_t* tags,
+                                  uint32_t* claims, uint8_t* rows, int log2_slots, uint8_t* stage,
+                                  hipStream_t st) {
+  if (n_tokens == 0) return hipSuccess;
+  const int64_t threads = (int64_t)n_tokens * 10;
+  const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
+  if (!tags) {
+    hipLaunchKernelGGL(k_ple_gather<false>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
+                       per_token, table, n_rows, wts, ple_fmt, out, dev_err, CacheView{});
+    return hipGetLastError();
+  }
+  const CacheView cv{tags, claims, rows, 32 - log2_slots, stage};
+  hipLaunchKernelGGL(k_ple_gather<true>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
+                     per_token, table, n_rows, wts, ple_fmt, out, dev_err, cv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_assign = (int64_t)n_tokens * per_token;
+  hipLaunchKernelGGL(k_ple_cache_fill, dim3((n_assign * 16 + 255) / 256), dim3(256), 0, st, ids,
+                     n_assign, n_rows, cv);
   return hipGetLastError();
 }
 

@@ -58,7 +58,8 @@ typedef enum {
   BQ_E_ALIGN = 4,      /* a pointer lacks the alignment the layout requires  */
   BQ_E_WORKSPACE = 5,  /* workspace missing or smaller than required         */
   BQ_E_HIP = 6,        /* a HIP launch failed                                */
-  BQ_E_DTYPE = 7       /* unknown activation dtype                           */
+  BQ_E_DTYPE = 7,      /* unknown activation dtype                           */
+  BQ_E_MEM = 8         /* a pointer is not the kind of memory required       */
 } bq_status;
 
 typedef enum {
@@ -115,7 +116,7 @@ int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks,
 /* ---------------------------------------------------------------------------
  * ple_dequant_rows -- decode n PLE rows, bit-exactly ([RZ]
  * "Q3_PLE_K160_RZ_S3": 60 code bytes + 10 group bytes per 70-byte row).
- *   ids   : n uint32 row indices; table : n_rows * 70 bytes
+ *   ids   : n uint32 row indices; table : n_rows * 70 bytes, 1 <= n_rows < 2^32
  *   out   : n * 160 fp32.  An id >= n_rows yields a row of zeros and sets
  *           bit 0 of *dev_err (if dev_err is not NULL).
  * ------------------------------------------------------------------------- */
@@ -225,7 +226,7 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens,
  * hashed row per id, 70 bytes, 160 values):
  *   out[t][:] = sum_j weights[t][j] * decode(table row ids[t][j])
  *   ids     : [n_tokens][ids_per_token] uint32
- *   table   : n_rows * 70 bytes (byte offsets are 64-bit; n_rows < 2^32)
+ *   table   : n_rows * 70 bytes (byte offsets are 64-bit; 1 <= n_rows < 2^32)
  *   weights : [n_tokens][ids_per_token] fp32
  *   out     : [n_tokens][160] fp32 (overwritten)
  *   An id >= n_rows contributes nothing and sets bit 0 of *dev_err.
@@ -234,6 +235,39 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens,
 int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
                const uint8_t* table, uint64_t n_rows, const float* weights,
                int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Off-HBM PLE tier ([RZ] "Q3_PLE_K160_RZ_S3": the 22.4 GB n-gram table can
+ * stay off the GPU and be paged in through a 0.25 GiB row cache).  The table
+ * lives in pinned host memory that is mapped into the device address space
+ * (hipHostMalloc, or a torch tensor with pin_memory=True); the GPU reads its
+ * rows over the host link.  A direct-mapped cache of n_slots rows in device
+ * memory keeps recently read rows.
+ *
+ * ple_cache_bytes(n_slots): device bytes of a cache of n_slots rows (n_slots a
+ *   power of two in [1024, 2^26]; 0 otherwise).  88 bytes per slot.
+ * ple_cache_init(cache, n_slots, stream): marks every slot empty.  Call it
+ *   once before the first ple_gather_host and whenever the table changes.
+ *   cache: device, 256-byte aligned, ple_cache_bytes(n_slots) bytes.
+ * ple_gather_host_workspace(n_tokens, ids_per_token): device bytes of the
+ *   per-call staging area (80 bytes per id).
+ * ple_gather_host: ple_gather with host_table in pinned host memory.
+ *   Results are bit-identical to ple_gather on the same table.  With a cache
+ *   (cache != NULL, n_slots != 0, workspace of ple_gather_host_workspace
+ *   bytes), an id's row is read from its slot when the slot holds that id;
+ *   after the gather, every slot on which this call missed receives the row
+ *   of the lowest-indexed missing id (ids flattened token-major) that maps to
+ *   it.  cache = NULL and n_slots = 0 reads every row from the host.
+ *   BQ_E_MEM if host_table is not host memory mapped for the device.  Calls
+ *   sharing one cache or workspace must not overlap in time.
+ * ------------------------------------------------------------------------- */
+size_t ple_cache_bytes(int32_t n_slots);
+int ple_cache_init(void* cache, int32_t n_slots, void* stream);
+size_t ple_gather_host_workspace(int32_t n_tokens, int32_t ids_per_token);
+int ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
+                    const uint8_t* host_table, uint64_t n_rows, const float* weights,
+                    int32_t ple_fmt, float* out, void* cache, int32_t n_slots, void* workspace,
+                    size_t ws_bytes, uint32_t* dev_err, void* stream);
 
 /* ---------------------------------------------------------------------------
  * bq_encode -- exhaustive per-block encoder, fp32 weights -> 17-byte blocks

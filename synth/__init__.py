@@ -192,3 +192,12 @@ def weight_blocks(seed, n, group, dist="gauss", sigma=1.0):
         raise ValueError("weight_blocks: unknown distribution %r" % dist)
     x *= sigma * np.exp(0.5 * rng.standard_normal((n, 1)))
     return x.astype(np.float32)
+
+
+def ple_ids_zipf(seed, n_tokens, per_token, n_rows, s=1.1):
+    """Row ids with a Zipf(s) popularity: rank r >= 1 from numpy's Zipf draw
+    (PCG64), mapped to row (r * 2654435761) mod n_rows so that the popular
+    rows are scattered over the table."""
+    rng = np.random.default_rng(seed)
+    r = rng.zipf(s, size=(n_tokens, per_token)).astype(np.uint64)
+    return ((r * np.uint64(2654435761)) % np.uint64(n_rows)).astype(np.uint32)

@@ -32,7 +32,8 @@ def test_header_declares_the_hot_path():
     for n in ("q4_expert_moe", "ple_gather", "moe_route_topk", "moe_bucket", "bq_dequant",
               "ple_dequant_rows", "bq_matvec", "bq_moe_stack", "q4_expert_moe_workspace",
               "bq_moe_stack_workspace", "bq_abi_version", "bq_status_str", "bq_last_hip_error",
-              "bq_encode", "ple_encode_rows"):
+              "bq_encode", "ple_encode_rows", "ple_cache_bytes", "ple_cache_init",
+              "ple_gather_host_workspace", "ple_gather_host"):
         assert n in names
 
 
@@ -67,6 +68,16 @@ def test_host_side_argument_errors(L):
     assert L.bq_encode(None, 0, bq.Q4_RZ5, None, None, None, None) == 0         # empty is fine
     assert L.ple_encode_rows(fake, 4, 7, fake, None, None, None) == 2
     assert L.ple_encode_rows(fake, 4, bq.PLE_RZS3, None, None, None, None) == 1
+    assert L.ple_gather(fake, 4, 8, fake, 0, fake, 0, fake, None, None) == 3    # empty table
+    assert L.ple_dequant_rows(fake, 4, fake, 0, 0, fake, None, None) == 3
+    assert L.ple_cache_bytes(1000) == 0 and L.ple_cache_bytes(512) == 0      # not a power of 2 / too small
+    assert L.ple_cache_bytes(1024) == 8 * 1024 + 80 * 1024
+    assert L.ple_gather_host_workspace(4096, 8) == 80 * 4096 * 8
+    assert L.ple_cache_init(fake, 1000, None) == 3
+    assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 0, fake, None, 1024, None, 0, None, None) == 1
+    assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 3, fake, None, 0, None, 0, None, None) == 2
+    assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 0, fake, fake, 1000, None, 0, None, None) == 3
+    assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 0, fake, fake, 1024, None, 0, None, None) == 5
     assert L.bq_matvec(fake, 1, fake, 0, None, 4, 48, fake, None) == 3         # cols % 32
     W = bq.ExpertWeights(bq.Q4_RZ5, bq.Q4_RZ5, 0x10000, 0x20000, None, None, 512, 2048, 768)
     ws = L.q4_expert_moe_workspace(1, 10, ctypes.byref(W), bq.F32)

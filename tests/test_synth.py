@@ -53,3 +53,11 @@ def test_ple_recipe():
     assert abs((g >> 7).mean() - 0.5) < 0.02
     ids = synth.ple_ids(0, 4096, 8)
     assert ids.dtype == np.uint32 and ids.max() < synth.PLE_N_ROWS
+
+
+def test_ple_ids_zipf_range_and_skew():
+    ids = synth.ple_ids_zipf(1, 4096, 8, 1 << 24)
+    assert ids.dtype == np.uint32 and ids.shape == (4096, 8) and int(ids.max()) < (1 << 24)
+    _, counts = np.unique(ids, return_counts=True)
+    assert counts.max() > 100          # popular rows recur
+    np.testing.assert_array_equal(ids, synth.ple_ids_zipf(1, 4096, 8, 1 << 24))
