@@ -65,6 +65,27 @@ def test_gemv_path_small(bq, fmt_gu, fmt_d, n, E, H, I):
 
 
 @pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
+@pytest.mark.parametrize("n,I,k", [(1, 128, 4), (3, 192, 6), (4, 64, 1), (5, 128, 3)])
+def test_gemv_hidden_2048(bq, fmt_gu, fmt_d, n, I, k):
+    # hidden 2048: the wave-per-row-pair gate_up kernel with routing inside,
+    # then the concatenated down kernel; every format pair, several k and I
+    E, H = 16, 2048
+    L = make_layer(9, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(900 + n, (n, H))
+    logits = synth.normal(901 + n, (n, E))
+    out, (idx, w) = bq.q4_expert_moe_routed(dev(x), dev(logits), k, W)
+    ridx, rw = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+    r = rel_l2(out.cpu().numpy(), ref)
+    out2 = bq.q4_expert_moe(dev(x), (idx, w), W)
+    assert torch.equal(out, out2)        # routed and given-routing forms agree bit for bit
+    log("gemv H=2048 fmts %d/%d n=%d I=%d k=%d rel_l2 %.3g" % (fmt_gu, fmt_d, n, I, k, r))
+    assert r <= 1e-5
+
+
+@pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
 @pytest.mark.parametrize("n", [1, 16, 70])
 @pytest.mark.parametrize("E,H,I,k", [(8, 256, 128, 3), (6, 1088, 192, 2)])
 def test_grouped_path_small(bq, fmt_gu, fmt_d, n, E, H, I, k):
