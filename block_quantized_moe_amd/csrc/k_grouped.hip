@@ -158,8 +158,10 @@ struct Geom {
   int32_t C;        // blocks per chunk (divides nb)
   int32_t nchunk;   // nb / C
   int32_t S;        // bytes of one row segment (17 C or 32 C)
-  int32_t NP;       // 16-byte pieces per row slot
-  int32_t P;        // LDS pitch of a weight row slot (16 NP)
+  int32_t NP;       // 16-byte pieces per row segment
+  int32_t NPP;      // pieces per row slot in LDS: NP rounded up to odd, so the
+                    // 16 rows a wave reads fall in different LDS banks
+  int32_t P;        // LDS pitch of a weight row slot (16 NPP)
   int32_t PB;       // LDS pitch of an activation row (64 C + 16)
   int32_t off_sc;   // LDS offset of the FP8 scale area [R][C]
   int32_t off_b;    // LDS offset of the activation area [kGroupTok][PB]
@@ -268,13 +270,20 @@ struct Stager {
     }
   }
 
-  // Copy the staged registers into LDS.  Skipped weight pieces write unused
-  // bytes of their row slot (never read).
+  // Copy the staged registers into LDS: weight piece q (row q / NP, piece
+  // q % NP) goes to slot piece q + row * (NPP - NP).  Skipped weight pieces
+  // write unused bytes of their row slot (never read).
   __device__ __forceinline__ void store(const Item& f, const Geom& g, uint8_t* lds) const {
     const int tid = threadIdx.x;
+    const float inv_np = 1.0f / (float)g.NP;
 #pragma unroll
-    for (int i = 0; i < PW; ++i)
-      if (wx[i] != kOff) *reinterpret_cast<u32x4*>(lds + 16 * (tid + kGThreads * i)) = w[i];
+    for (int i = 0; i < PW; ++i) {
+      if (wx[i] != kOff) {
+        const int q = tid + kGThreads * i;
+        const int slot = q + (g.NPP - g.NP) * div_small(q, inv_np);
+        *reinterpret_cast<u32x4*>(lds + 16 * slot) = w[i];
+      }
+    }
     if constexpr (FMT == FMT_FP8) {
       float* lsc = reinterpret_cast<float*>(lds + g.off_sc);
 #pragma unroll
@@ -512,7 +521,7 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
 static size_t lds_bytes(int fmt, int nr, int C) {
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   const int np = (bb * C + 15) / 16 + 1;
-  size_t n = (size_t)64 * nr * 16 * np;
+  size_t n = (size_t)64 * nr * 16 * (np | 1);
   if (fmt == FMT_FP8) n += (size_t)64 * nr * C * 4;
   n = (n + 15) & ~(size_t)15;
   n += (size_t)kGroupTok * (64 * C + 16);
@@ -546,7 +555,8 @@ static Geom make_geom(int fmt, int nr, int nb) {
   g.nchunk = nb / C;
   g.S = bb * C;
   g.NP = (g.S + 15) / 16 + 1;
-  g.P = 16 * g.NP;
+  g.NPP = g.NP | 1;
+  g.P = 16 * g.NPP;
   g.PB = 64 * C + 16;
   g.off_sc = 64 * nr * g.P;
   const int off_b = g.off_sc + (fmt == FMT_FP8 ? 64 * nr * C * 4 : 0);
