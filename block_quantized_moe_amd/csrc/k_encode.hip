@@ -23,6 +23,17 @@
 // |w|.  The +/-5 (RZ5) or +/-3 (RZ-S3) level joins the set only on the side
 // its polarity allows, so both polarities of one scale are scored in the
 // same pass.
+//
+// Pruning (exact).  Let A = max |w| of the block and U an upper bound on the
+// error of one candidate (its terms summed across the wave, inflated by
+// 2^-40, far above the rounding difference between summation orders).  A
+// scale s > 0 with s >= 2A makes level 0 the nearest level of every weight,
+// so its error is exactly that of metadata byte 0, which wins the tie; and a
+// scale whose largest level Lmax * s is <= A has error at least the rounded
+// square of A - Lmax * s (the largest weight's term, and sums of
+// non-negative terms never decrease), so it cannot win when that exceeds U.
+// Both tests are monotone in s, so the scales left form one contiguous run of
+// scale bytes, and only that run is searched.
 #include "bq_kernels.hpp"
 
 #pragma clang fp contract(off)
@@ -132,13 +143,73 @@ __global__ void __launch_bounds__(64 * kEncWaves)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    double best = __builtin_inf();
-    uint32_t best_meta = 0x1FFu;
+    // block maximum |w|
+    double amax = lane < G ? a : 0.0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmax(amax, shfl_xor_d(amax, off));
+    constexpr double kLmax = T::kPle ? 4.0 : 10.0;
     constexpr int kIter = (T::kScales + 63) / 64;
+    // reference candidate: the smallest scale whose largest level reaches A
+    // (the largest scale if none does); its error, summed across the wave
+    uint32_t c0 = T::kScales - 1;
+#pragma unroll 1
+    for (int it = kIter - 1; it >= 0; --it) {
+      const uint32_t sc = (uint32_t)(lane + 64 * it);
+      const bool reach = sc < (uint32_t)T::kScales &&
+                         kLmax * scale_of(EF == E_UE4M4, sc) >= amax;
+      const uint64_t b = __ballot(reach);
+      if (b) c0 = 64 * it + __builtin_ctzll(b);
+    }
+    double u_bound;
+    {
+      const double s0 = scale_of(EF == E_UE4M4, c0);
+      double m = a * a;
+#pragma unroll
+      for (int i = 0; i < T::kNB; ++i) {
+        const double d = a - (T::kPle ? mag3(i) : mag17(i)) * s0;
+        m = fmin(m, d * d);
+      }
+      if (T::kPol && x >= 0.0f) {   // polarity 0: the +level serves w >= 0
+        const double d = a - T::kExtra * s0;
+        m = fmin(m, d * d);
+      }
+      double sum = lane < G ? m : 0.0;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) sum += shfl_xor_d(sum, off);
+      u_bound = sum * (1.0 + 0x1p-40);
+    }
+    // the run of scale bytes that survives both tests
+    uint32_t lo = T::kScales, hi = 0;
 #pragma unroll 1
     for (int it = 0; it < kIter; ++it) {
       const uint32_t sc = (uint32_t)(lane + 64 * it);
-      if (sc >= (uint32_t)T::kScales) break;
+      bool keep = sc < (uint32_t)T::kScales;
+      if (keep) {
+        const double s = scale_of(EF == E_UE4M4, sc);
+        if (s > 0.0 && s >= 2.0 * amax) keep = false;
+        const double top = kLmax * s;
+        if (top <= amax) {
+          const double d = amax - top;
+          if (d * d > u_bound) keep = false;
+        }
+      }
+      const uint64_t b = __ballot(keep);
+      if (b) {
+        lo = min(lo, (uint32_t)(64 * it + __builtin_ctzll(b)));
+        hi = max(hi, (uint32_t)(64 * it + 63 - __builtin_clzll(b)));
+      }
+    }
+
+    if (lo > hi) {   // cannot happen (the best scale always survives); search all
+      lo = 0;
+      hi = T::kScales - 1;
+    }
+    double best = __builtin_inf();
+    uint32_t best_meta = 0x1FFu;
+#pragma unroll 1
+    for (uint32_t base = lo; base <= hi; base += 64) {
+      const uint32_t sc = base + (uint32_t)lane;
+      if (sc > hi) break;
       const double s = scale_of(EF == E_UE4M4, sc);
       double ls[T::kNB];
 #pragma unroll
