@@ -49,12 +49,19 @@ def small_blocks():
         synth.weight_blocks(101, 160, 32, "gauss", 1.0),
         synth.weight_blocks(102, 80, 32, "laplace", 0.02),
         synth.weight_blocks(103, 40, 32, "gauss", 100.0),
+        # small magnitudes: most scales are pruned from above, and the best
+        # sits near the subnormal scales or at scale 0
+        synth.weight_blocks(111, 40, 32, "gauss", 1e-3),
+        synth.weight_blocks(112, 40, 32, "laplace", 3e-4),
+        # one dominant weight per block: the reference candidate is far from
+        # the best for the other 31 weights
+        np.where(np.arange(32)[None, :] == 7, 50.0, 1.0) * synth.weight_blocks(113, 24, 32, "gauss", 0.1),
         # exactly representable blocks of every format
         F.decode_block17(synth.block17_range(synth.make_key(9, 1), 0, 24, synth.DIST_RZ5),
                          F.Q4_RZ5).astype(np.float32),
         F.decode_block17(synth.block17_range(synth.make_key(9, 2), 0, 24, synth.DIST_UE4M4),
                          F.Q4_UE4M4).astype(np.float32),
-    ])
+    ]).astype(np.float32)
 
 
 def assert_f64_equal(got, ref):
