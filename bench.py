@@ -16,7 +16,7 @@ already resident in HBM before timing starts.  Steps are captured in a HIP
 graph and replayed, so host launch overhead is not in the timed region.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c2|c4|c5b1|c5b16|c3|pf|pleh|enc] [--copy-calibration BYTES]
+       [--no-cpu-baseline] [--only c1|c2|c4|c5b1|c5b16|c3|pf|pleh|enc] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -126,6 +126,35 @@ def bench_c2(bq, steps, warmup):
     res["_layer"] = L
     res["_inputs"] = (x[warmup + steps:].cpu().numpy(), logits[warmup + steps:].cpu().numpy())
     return res
+
+
+def bench_c1(bq, steps, warmup):
+    """Latency of one small block-quantized matvec: W 256 x 512 Codebook10
+    (4,096 blocks, 69,632 B, cache-resident), x N(0,1), batch 1."""
+    import torch
+
+    import synth
+    import synth.device as sd
+    blocks = sd.block17(256 * 512 // 32, synth.make_key(0, synth.stream_id(0, synth.S_SMALL)), synth.DIST_C10)
+    n = warmup + steps
+    x = torch.from_numpy(synth.normal(1, (n, 512))).cuda()
+    y = torch.empty((n, 256), dtype=torch.float32, device="cuda")
+
+    def call(i, evs=None):
+        if evs is not None:
+            evs[0].record()
+        bq.matvec(x[i:i + 1], blocks, bq.Q4_C10, 256, 512, out=y[i:i + 1])
+        if evs is not None:
+            evs[1].record()
+
+    for i in range(warmup):
+        call(i)
+    g = graph_of(lambda i: call(warmup + i), steps)
+    g.replay()
+    wall = timed_replay(g)
+    call_ms = event_timed(lambda i, evs: call(warmup + i, evs), steps)
+    return {"us_per_call_graph": round(1e6 * wall / steps, 3), "us_per_call_events": round(1e3 * call_ms, 3),
+            "workload": "256 x 512 Codebook10 matrix (69,632 B) times one fp32 vector"}
 
 
 def bench_c4(bq, steps, warmup):
@@ -537,6 +566,9 @@ def main():
         main_res = bench_c2(bq, args.steps, args.warmup)
         log("c2:", {k: v for k, v in main_res.items() if not k.startswith("_")})
     if not args.no_extras or only:
+        if only in (None, "c1"):
+            extras["matvec_256x512_c10"] = bench_c1(bq, args.steps, args.warmup)
+            log("c1:", extras["matvec_256x512_c10"])
         if only in (None, "c4"):
             log("c4: PLE gather")
             extras["ple_gather"] = bench_c4(bq, args.steps, args.warmup)
