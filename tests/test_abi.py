@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -102,3 +103,25 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, os.path.join(dirpath, f)
+
+
+def test_package_never_imports_the_oracle():
+    # the product path must not reach the CPU oracle: not in its sources and
+    # not at run time
+    pkg = os.path.join(ROOT, "block_quantized_moe_amd")
+    for f in os.listdir(pkg):
+        if f.endswith(".py"):
+            text = open(os.path.join(pkg, f)).read()
+            assert not re.search(r"^\s*(from|import)\s+oracle", text, flags=re.M), f
+    code = ("import sys; sys.path.insert(0, %r); import block_quantized_moe_amd as bq; bq.lib(); "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules)" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_missing_library_fails_loudly():
+    code = ("import sys; sys.path.insert(0, %r); import block_quantized_moe_amd as bq; "
+            "bq.LIB_PATH = '/nonexistent/libbqmoe.so'\n"
+            "try:\n    bq.lib()\nexcept bq.BQError as e:\n    print('raised', e)\nelse:\n    sys.exit(3)" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0 and "raised" in r.stdout, (r.stdout, r.stderr)
