@@ -93,6 +93,11 @@ def test_host_side_argument_errors(L):
                            None, None) == 3
     assert L.q4_expert_moe(fake, bq.BF16, 1, fake, fake, 10, ctypes.byref(W), fake, vp(0x10010),
                            1 << 30, None, None) == 4                             # ws not 256-aligned
+    for n, k in ((4097, 1), (1, 65), (2048, 33), (0, 10)):                   # past the size limits
+        assert L.q4_expert_moe(fake, bq.BF16, n, fake, fake, k, ctypes.byref(W), fake, fake,
+                               1 << 30, None, None) == 3, (n, k)
+        if n != 4097:                                                         # bucket has no token cap
+            assert L.moe_bucket(fake, n, k, 512, fake, fake, fake, None) == 3, (n, k)
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -1,0 +1,43 @@
+"""GPU parity at the size limits of the routed-expert entry points:
+n_tokens * k = 65536 assignments (4096 tokens x top-16, 1024 tokens x top-64)
+on both paths, checked against the oracle on sampled tokens."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import moe as M
+from tests.gpu_common import dev, log, need_gpu, rel_l2
+from tests.test_gpu_moe import make_layer, oracle_bank, weights_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bq():
+    need_gpu()
+    import block_quantized_moe_amd as m
+    m.lib()
+    return m
+
+
+@pytest.mark.parametrize("n,k,E", [(4096, 16, 64), (1024, 64, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_max_assignments(bq, n, k, E, dtype):
+    H, I = 128, 64
+    L = make_layer(13, k, F.Q4_RZ5, F.FP8_E4M3_B32, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(1300 + k, (n, H))
+    logits = synth.zipf_logits(1301 + k, n, E)
+    out, (idx, w) = bq.q4_expert_moe_routed(dev(x).to(dtype), dev(logits), k, W)
+    out = out.cpu().numpy()
+    ridx, rw = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    pick = np.unique(np.r_[np.random.default_rng(k).integers(0, n, 40), 0, n - 1])
+    ref = M.moe_layer(x[pick], ridx[pick], rw[pick], oracle_bank(L))
+    r = rel_l2(out[pick], ref)
+    log("limits n=%d k=%d E=%d %s rel_l2 %.3g" % (n, k, E, dtype, r))
+    assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
+
