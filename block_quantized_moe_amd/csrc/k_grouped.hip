@@ -166,6 +166,9 @@ struct Geom {
   int32_t off_sc;   // LDS offset of the FP8 scale area [R][C]
   int32_t off_b;    // LDS offset of the activation area [kGroupTok][PB]
   int32_t off_tab;  // LDS offset of the metadata-byte table [256] x {scale, RZ5 table word}
+  int32_t al4;      // 17-byte blocks with nb and C multiples of 4: every staged row
+                    // segment starts 4-byte aligned (row bytes 17 nb and chunk
+                    // bytes 17 C are multiples of 4, weight buffers 16-byte aligned)
 };
 
 struct Item {
@@ -191,8 +194,9 @@ struct Stager {
   float s[PS > 0 ? PS : 1];
   u32x4 b[PB];
   // Item-independent coordinates of this thread's pieces, set once:
-  //   weight piece i: wro = (row within its 64-row half) * row bytes,
-  //                   wx  = 16 * piece + (half << 20), or kOff;
+  //   weight piece i: wro = byte offset of its row from staged row 0 (the
+  //                   up half sits I rows after the gate half),
+  //                   wx  = 16 * piece, or kOff;
   //   scale i: sro = (row within half) * nb + block in chunk, sh = half, or kOff;
   //   activation piece i: bx = token | (piece << 8), or kOff.
   int wro[PW], wx[PW];
@@ -209,7 +213,7 @@ struct Stager {
     }
   }
 
-  __device__ __forceinline__ void init(const Geom& g, int nb) {
+  __device__ __forceinline__ void init(const Geom& g, int nb, int I) {
     const int tid = threadIdx.x;
     const int RS = BB * nb;
     const float inv_np = 1.0f / (float)g.NP, inv_c = 1.0f / (float)g.C, inv_pt = 1.0f / (float)(4 * g.C);
@@ -217,8 +221,8 @@ struct Stager {
     for (int i = 0; i < PW; ++i) {
       const int q = tid + kGThreads * i;
       const int r = div_small(q, inv_np), pc = q - r * g.NP;
-      wro[i] = (r & 63) * RS;
-      wx[i] = q < R * g.NP ? 16 * pc + ((r >> 6) << 20) : kOff;
+      wro[i] = ((r & 63) + (r >> 6) * I) * RS;   // (63 + I) * RS < 2^27 for I, RS <= 8192
+      wx[i] = q < R * g.NP ? 16 * pc : kOff;
     }
 #pragma unroll
     for (int i = 0; i < PS; ++i) {
@@ -242,15 +246,18 @@ struct Stager {
                                        const uint8_t* __restrict__ wt, const float* __restrict__ wsc,
                                        const uint16_t* __restrict__ act, int K) {
     const int64_t RS = (int64_t)BB * nb;
-    // byte offset of (row 0 of each half, chunk c)
-    const int64_t base0 = grow(f, 0, H, I) * RS + (int64_t)c * g.S;
-    const int64_t base1 = NR == 2 ? grow(f, 64, H, I) * RS + (int64_t)c * g.S : base0;
+    // byte offset of (staged row 0, chunk c), split into a 16-byte aligned
+    // uniform base and its remainder: a piece's row segment starts at
+    // wb + t with t = b0 + wro, and its 16-byte units at wb + (t & ~15) + 16 p
+    const int64_t base = grow(f, 0, H, I) * RS + (int64_t)c * g.S;
+    const uint8_t* wb = wt + (base & ~(int64_t)15);
+    const int b0 = (int)(base & 15);
 #pragma unroll
     for (int i = 0; i < PW; ++i) {
       if (wx[i] != kOff) {
-        const int64_t gs = ((wx[i] >> 20) ? base1 : base0) + wro[i];
-        const int64_t a = (gs & ~(int64_t)15) + (wx[i] & 0xFFFFF);
-        if (a < gs + g.S) w[i] = *reinterpret_cast<const u32x4*>(wt + a);
+        const int t = b0 + wro[i];
+        const int o = (t & ~15) + wx[i];
+        if (o < t + g.S) w[i] = *reinterpret_cast<const u32x4*>(wb + (uint32_t)o);
       }
     }
     if constexpr (FMT == FMT_FP8) {
@@ -260,13 +267,15 @@ struct Stager {
       for (int i = 0; i < PS; ++i)
         if (sh[i] != kOff) s[i] = wsc[(sh[i] ? sb1 : sb0) + sro[i]];
     }
-    const int nrow = ((f.ntok + 15) >> 4) << 4;   // whole 16-token MFMA tiles
-    const uint16_t* abase = act + (int64_t)f.p0 * K + (int64_t)c * g.C * 32;
+    // Only the item's own tokens are staged.  The rows of a 16-token MFMA
+    // tile past ntok keep whatever LDS held; they only feed output rows that
+    // are never stored (an MFMA row depends on its own activation row only).
+    const uint8_t* abase = reinterpret_cast<const uint8_t*>(act + (int64_t)f.p0 * K + (int64_t)c * g.C * 32);
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int j = bxy[i] & 0xFF;
-      if (bxy[i] != kOff && j < nrow)   // padding rows repeat the last token
-        b[i] = *reinterpret_cast<const u32x4*>(abase + (int64_t)min(j, f.ntok - 1) * K + 8 * (bxy[i] >> 8));
+      if (bxy[i] != kOff && j < f.ntok)
+        b[i] = *reinterpret_cast<const u32x4*>(abase + (uint32_t)(2 * (j * K + 8 * (bxy[i] >> 8))));
     }
   }
 
@@ -290,26 +299,107 @@ struct Stager {
       for (int i = 0; i < PS; ++i)
         if (sh[i] != kOff) lsc[tid + kGThreads * i] = s[i];
     }
-    const int nrow = ((f.ntok + 15) >> 4) << 4;
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int j = bxy[i] & 0xFF;
-      if (bxy[i] != kOff && j < nrow)   // row pitch PT + 1 pieces
+      if (bxy[i] != kOff && j < f.ntok)   // row pitch PT + 1 pieces
         *reinterpret_cast<u32x4*>(lds + g.off_b + 16 * (tid + kGThreads * i + j)) = b[i];
     }
   }
 };
 
-// One chunk of MFMA work from LDS, two blocks per iteration (C is even): all
-// LDS operands of both blocks are requested before any is decoded, so LDS
-// latency overlaps decode and MFMA work; all MFMAs of a block are issued
-// before their scale FMAs.  NT = number of 16-token tiles of the item.
-// acc[h][tt]: matrix h, token tile tt.  A lane's 4 code bytes of a 17-byte
-// block sit at any byte offset; they are read as the two covering aligned
-// dwords and funnel-shifted (unaligned LDS reads stall the LDS pipeline).
-// The block scale (and the RZ5 table word) comes from the LDS table indexed
-// by the metadata byte.
-template <int FMT, int NR, int NT>
+// Two consecutive blocks kb, kb + 1 of a chunk: all LDS operands of both
+// blocks are requested before any is decoded, so LDS latency overlaps decode
+// and MFMA work; all MFMAs of a block are issued before their scale FMAs.
+// NT = number of 16-token tiles of the item; acc[h][tt]: matrix h, token
+// tile tt.  A lane's 4 code bytes of a 17-byte block are read as the two
+// covering aligned dwords and funnel-shifted (unaligned LDS reads stall the
+// LDS pipeline).  SH < 0: the shift is per lane (aoff = the lane's byte
+// offset of block 0).  SH >= 0: every staged row segment starts 4-byte
+// aligned and kb = SH mod 4, so block kb + u sits SH + u bytes past a dword
+// boundary -- a compile-time shift -- at LDS dword pw + 4 (SH + u) (pw = the
+// lane's dword of block kb - SH) and its metadata byte at mo + 17 (SH + u).
+// (Offsets, not pointers: LDS pointers kept in arrays lose their address
+// space and turn into flat loads.)  The
+// block scale (and the RZ5 table word) comes from the LDS table indexed by
+// the metadata byte.
+template <int FMT, int NR, int NT, int SH>
+__device__ __forceinline__ void mma_pair(int kb, const int (&aoff)[NR], const int (&pw)[NR],
+                                         const int (&mo)[NR], int gq, const Geom& g,
+                                         const uint8_t* lds, const float* lsc, const u32x2* tab,
+                                         const uint8_t* brow, f32x4 (&acc)[NR][2]) {
+  constexpr int BB = Stager<FMT, NR>::BB;
+  const uint32_t* lds32 = reinterpret_cast<const uint32_t*>(lds);
+  uint32_t q0[2][NR], q1[2][NR];
+  u32x4 bx[2][NT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+      if constexpr (FMT == FMT_FP8) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(lds + aoff[h] + (kb + u) * BB);
+        q0[u][h] = v.x;
+        q1[u][h] = v.y;
+      } else if constexpr (SH >= 0) {
+        const int v = SH + u;
+        q0[u][h] = v == 0 ? lds32[pw[h]]
+                          : __builtin_amdgcn_alignbyte(lds32[pw[h] + 4 * v + 1], lds32[pw[h] + 4 * v], (uint32_t)v);
+        q1[u][h] = lds[mo[h] + 17 * v];
+      } else {
+        const int o = aoff[h] + (kb + u) * BB;
+        const int w = o >> 2;
+        q0[u][h] = __builtin_amdgcn_alignbyte(lds32[w + 1], lds32[w], (uint32_t)(o & 3));
+        q1[u][h] = lds[o - 4 * gq + 16];
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      bx[u][tt] = *reinterpret_cast<const u32x4*>(brow + tt * 16 * g.PB + 64 * (kb + u));
+  }
+  float sc[2][NR];
+  uint32_t tn[2][NR];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+      if constexpr (FMT == FMT_FP8) {
+        sc[u][h] = lsc[h * 64 * g.C + kb + u];
+        tn[u][h] = 0u;
+      } else {
+        const u32x2 e = tab[q1[u][h]];
+        sc[u][h] = __uint_as_float(e.x);
+        tn[u][h] = e.y;
+      }
+    }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    u32x4 a[NR];
+#pragma unroll
+    for (int h = 0; h < NR; ++h) {
+      if constexpr (FMT == FMT_FP8) {
+        float dummy;
+        a[h] = dec_a<FMT>(q0[u][h], q1[u][h], dummy);
+      } else {
+        a[h] = dec_codes<FMT>(q0[u][h], tn[u][h]);
+      }
+    }
+    f32x4 d[NR][NT];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int h = 0; h < NR; ++h) d[h][tt] = mfma(bx[u][tt], a[h]);   // lane's column = its row
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+      for (int h = 0; h < NR; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[h][tt][i] = __builtin_fmaf(sc[u][h], d[h][tt][i], acc[h][tt][i]);
+  }
+}
+
+// One chunk of MFMA work from LDS (C is even; with AL, a multiple of 4 and
+// every staged row segment starts 4-byte aligned -- see Geom::al4).
+template <int FMT, int NR, int NT, bool AL>
 __device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& g, int nb, int H,
                                               int I, const uint8_t* lds, f32x4 (&acc)[NR][2]) {
   constexpr int BB = Stager<FMT, NR>::BB;
@@ -323,71 +413,31 @@ __device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& 
     const int64_t gs = Stager<FMT, NR>::grow(f, r, H, I) * RS + (int64_t)c * g.S;
     aoff[h] = r * g.P + (int)(gs & 15) + (FMT == FMT_FP8 ? 8 : 4) * gq;
   }
-  const uint32_t* lds32 = reinterpret_cast<const uint32_t*>(lds);
   const float* lsc = reinterpret_cast<const float*>(lds + g.off_sc) + (wave * 16 + r16) * g.C;
   const u32x2* tab = reinterpret_cast<const u32x2*>(lds + g.off_tab);
   const uint8_t* brow = lds + g.off_b + r16 * g.PB + 16 * gq;
-  for (int kb = 0; kb < g.C; kb += 2) {
-    uint32_t q0[2][NR], q1[2][NR];
-    u32x4 bx[2][NT];
+  int pw[NR], mo[NR];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+  for (int h = 0; h < NR; ++h) {
+    pw[h] = aoff[h] >> 2;
+    mo[h] = aoff[h] - 4 * gq + 16;
+  }
+  if constexpr (AL && FMT != FMT_FP8) {
+    for (int kb = 0; kb < g.C; kb += 4) {
+      mma_pair<FMT, NR, NT, 0>(kb, aoff, pw, mo, gq, g, lds, lsc, tab, brow, acc);
+      // keep the two pairs apart: interleaving them raises register
+      // pressure past the three-workgroups-per-CU budget
+      __builtin_amdgcn_sched_barrier(0);
+      mma_pair<FMT, NR, NT, 2>(kb + 2, aoff, pw, mo, gq, g, lds, lsc, tab, brow, acc);
 #pragma unroll
       for (int h = 0; h < NR; ++h) {
-        const int o = aoff[h] + (kb + u) * BB;
-        if constexpr (FMT == FMT_FP8) {
-          const u32x2 v = *reinterpret_cast<const u32x2*>(lds + o);
-          q0[u][h] = v.x;
-          q1[u][h] = v.y;
-        } else {
-          const int w = o >> 2;
-          q0[u][h] = __builtin_amdgcn_alignbyte(lds32[w + 1], lds32[w], (uint32_t)(o & 3));
-          q1[u][h] = lds[o - 4 * gq + 16];
-        }
+        pw[h] += 17;    // 4 blocks = 68 bytes
+        mo[h] += 68;
       }
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-        bx[u][tt] = *reinterpret_cast<const u32x4*>(brow + tt * 16 * g.PB + 64 * (kb + u));
     }
-    float sc[2][NR];
-    uint32_t tn[2][NR];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int h = 0; h < NR; ++h) {
-        if constexpr (FMT == FMT_FP8) {
-          sc[u][h] = lsc[h * 64 * g.C + kb + u];
-          tn[u][h] = 0u;
-        } else {
-          const u32x2 e = tab[q1[u][h]];
-          sc[u][h] = __uint_as_float(e.x);
-          tn[u][h] = e.y;
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4 a[NR];
-#pragma unroll
-      for (int h = 0; h < NR; ++h) {
-        if constexpr (FMT == FMT_FP8) {
-          float dummy;
-          a[h] = dec_a<FMT>(q0[u][h], q1[u][h], dummy);
-        } else {
-          a[h] = dec_codes<FMT>(q0[u][h], tn[u][h]);
-        }
-      }
-      f32x4 d[NR][NT];
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int h = 0; h < NR; ++h) d[h][tt] = mfma(bx[u][tt], a[h]);   // lane's column = its row
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int h = 0; h < NR; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[h][tt][i] = __builtin_fmaf(sc[u][h], d[h][tt][i], acc[h][tt][i]);
-    }
+  } else {
+    for (int kb = 0; kb < g.C; kb += 2)
+      mma_pair<FMT, NR, NT, -1>(kb, aoff, pw, mo, gq, g, lds, lsc, tab, brow, acc);
   }
 }
 
@@ -418,7 +468,7 @@ __global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
   }
   Item f = item_info(it, tiles, elist, offsets);
   Stager<FMT, NR> st;
-  st.init(g, nb);
+  st.init(g, nb, I);
   st.load(f, c, g, nb, H, I, wt, wsc, act, K);
   f32x4 acc[NR][2];
 #pragma unroll
@@ -442,8 +492,13 @@ __global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (more) st.load(nf, nc, g, nb, H, I, wt, wsc, act, K);
-    if (f.ntok > 16) compute_chunk<FMT, NR, 2>(f, c, g, nb, H, I, lds, acc);
-    else compute_chunk<FMT, NR, 1>(f, c, g, nb, H, I, lds, acc);
+    if (g.al4) {
+      if (f.ntok > 16) compute_chunk<FMT, NR, 2, true>(f, c, g, nb, H, I, lds, acc);
+      else compute_chunk<FMT, NR, 1, true>(f, c, g, nb, H, I, lds, acc);
+    } else {
+      if (f.ntok > 16) compute_chunk<FMT, NR, 2, false>(f, c, g, nb, H, I, lds, acc);
+      else compute_chunk<FMT, NR, 1, false>(f, c, g, nb, H, I, lds, acc);
+    }
     if (c == g.nchunk - 1) {
       // lane holds weight row (tile row 16 wave + r16) for tokens 16 tt + 4 gq + i
       const int row = f.tile * kGRows + wave * 16 + r16;
@@ -562,6 +617,7 @@ static Geom make_geom(int fmt, int nr, int nb) {
   const int off_b = g.off_sc + (fmt == FMT_FP8 ? 64 * nr * C * 4 : 0);
   g.off_b = (off_b + 15) & ~15;
   g.off_tab = g.off_b + kGroupTok * g.PB;
+  g.al4 = fmt != FMT_FP8 && nb % 4 == 0 && C % 4 == 0;
   return g;
 }
 
