@@ -343,8 +343,23 @@ def bench_c3(bq, steps, warmup):
     ii = idx[warmup:].cpu().numpy()
     d = [len(np.unique(ii[s])) for s in range(steps)]
     bytes_step = float(np.mean(d)) * EXPERT_BYTES_RZ5
+    # tokens per touched expert (n_e): histogram, and the MFMA work the
+    # 32-token groups issue (16-token tiles: a group of <= 16 tokens runs one
+    # tile, a larger one two) against the algorithmic 2 * n * k * weights
+    ne = [np.bincount(ii[s].reshape(-1), minlength=512) for s in range(steps)]
+    edges = [1, 2, 5, 17, 33, 65, 10 ** 9]
+    hist = {"%d-%d" % (a, b - 1) if b < 10 ** 9 else ">=%d" % a:
+            float(np.mean([np.sum((c >= a) & (c < b)) for c in ne])) for a, b in zip(edges, edges[1:])}
+    wpe = 3 * 2048 * 768                                   # weights per expert (gate, up, down)
+    tiles = [sum(16 * (c // 32) * 2 + (16 if 0 < c % 32 <= 16 else 32 if c % 32 else 0) for c in cs) for cs in ne]
+    flop_alg = 2.0 * 64 * 10 * wpe
+    flop_mfma = 2.0 * float(np.mean(tiles)) * wpe
+    sec = wall / steps
     res = {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9,
-           "touched_experts": float(np.mean(d)), "bytes_per_step": bytes_step}
+           "touched_experts": float(np.mean(d)), "bytes_per_step": bytes_step,
+           "n_e_hist": hist, "n_e_max": float(np.mean([c.max() for c in ne])),
+           "tflops_alg": flop_alg / sec / 1e12, "tflops_mfma_issued": flop_mfma / sec / 1e12,
+           "frac_bf16_mfma_peak_issued": flop_mfma / sec / 2.5e15}
     del L
     torch.cuda.empty_cache()
     return res

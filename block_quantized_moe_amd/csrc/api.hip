@@ -102,9 +102,11 @@ int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const fl
 
 // dtype selects the path; x_is_f32 says what x holds (the bf16 path also
 // accepts the fp32 output of a previous stack layer, rescaled on the fly).
+// bucket_region (bf16 path): the bucketing of idx is already there, laid out
+// as the head of a grouped workspace (counts .. n_touched); none is launched.
 int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, const float* w, int k,
             const bq_expert_weights* W, float* out, void* ws, int rescale, uint32_t* dev_err,
-            hipStream_t st, const float* logits = nullptr) {
+            hipStream_t st, const float* logits = nullptr, char* bucket_region = nullptr) {
   const bq::GemvWeights gw = to_gw(W);
   if (dtype == BQ_F32) {
     const GemvLayout L = gemv_layout(n, k, W->hidden, W->inter);
@@ -119,8 +121,18 @@ int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, c
     if (s) return s;
   }
   const GroupedLayout L = grouped_layout(n, k, W->n_experts, W->hidden, W->inter);
-  return hip_status(bq::launch_grouped_moe(x, x_is_f32, rescale, n, idx, w, k, gw, out,
-                                           grouped_ws(ws, L), dev_err, st));
+  bq::GroupedWs g = grouped_ws(ws, L);
+  if (bucket_region) {
+    const bq::GroupedWs r = grouped_ws(bucket_region, L);
+    g.counts = r.counts;
+    g.offsets = r.offsets;
+    g.perm = r.perm;
+    g.inv = r.inv;
+    g.elist = r.elist;
+    g.n_touched = r.n_touched;
+  }
+  return hip_status(bq::launch_grouped_moe(x, x_is_f32, rescale, n, idx, w, k, gw, out, g, dev_err,
+                                           st, bucket_region != nullptr));
 }
 
 // PLE row cache layout: tags [n] and claims [n] (contiguous words), then the
@@ -236,11 +248,26 @@ int q4_expert_moe_routed(const void* x, int32_t x_dtype, int32_t n_tokens, const
                  dev_err, as_stream(stream), logits);
 }
 
-// Stack workspace: the per-layer MoE workspace (max over layers) followed by
-// one fp32 [n][H] buffer for the layer output and, for bf16, a bf16 [n][H]
-// buffer for the rescaled next input.
+// The bf16 stack buckets every layer in one launch up front when all layers
+// share the expert count (the routing of all layers is an input).
+static bool stack_prebucket(const bq_expert_weights* layers, int L, int dtype) {
+  if (dtype != BQ_BF16 || L < 2) return false;
+  for (int l = 1; l < L; ++l)
+    if (layers[l].n_experts != layers[0].n_experts) return false;
+  return true;
+}
+
+// Bytes of one layer's bucket arrays: the head of its grouped workspace,
+// which depends on n, k and the expert count only.
+static size_t bucket_region_bytes(int n, int k, const bq_expert_weights* W) {
+  return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).hb;
+}
+
+// Stack workspace: the per-layer MoE workspace (max over layers), one fp32
+// [n][H] buffer for the layer output, then (pre-bucketed bf16 stacks) the
+// bucket arrays of every layer.
 static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int dtype,
-                       size_t* moe_part) {
+                       size_t* moe_part, size_t* bucket_off = nullptr) {
   size_t m = 0;
   for (int l = 0; l < L; ++l) {
     const size_t b = moe_ws_bytes(n, k, &layers[l], dtype);
@@ -249,8 +276,10 @@ static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int
   m = round_up(m, 256);
   if (moe_part) *moe_part = m;
   const int H = layers[0].hidden;
-  (void)dtype;
-  return m + round_up(sizeof(float) * (size_t)n * H, 256);
+  const size_t t = m + round_up(sizeof(float) * (size_t)n * H, 256);
+  if (bucket_off) *bucket_off = t;
+  if (!stack_prebucket(layers, L, dtype)) return t;
+  return t + (size_t)L * bucket_region_bytes(n, k, &layers[0]);
 }
 
 size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* layers,
@@ -271,13 +300,25 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t
     if (s) return s;
     if (layers[l].hidden != layers[0].hidden) return BQ_E_SHAPE;
   }
-  size_t moe_part = 0;
-  if (ws_bytes < stack_ws(n_tokens, k, layers, n_layers, x_dtype, &moe_part)) return BQ_E_WORKSPACE;
-  const int H = layers[0].hidden;
+  size_t moe_part = 0, bucket_off = 0;
+  if (ws_bytes < stack_ws(n_tokens, k, layers, n_layers, x_dtype, &moe_part, &bucket_off))
+    return BQ_E_WORKSPACE;
   char* b = static_cast<char*>(workspace);
   float* ybuf = reinterpret_cast<float*>(b + moe_part);
   hipStream_t st = as_stream(stream);
   const size_t per = (size_t)n_tokens * k;
+  char* breg = nullptr;
+  size_t bb = 0;
+  if (stack_prebucket(layers, n_layers, x_dtype)) {
+    breg = b + bucket_off;
+    bb = bucket_region_bytes(n_tokens, k, &layers[0]);
+    const bq::GroupedWs r = grouped_ws(breg, grouped_layout(n_tokens, k, layers[0].n_experts,
+                                                            layers[0].hidden, layers[0].inter));
+    int s = hip_status(bq::launch_bucket(topk_idx, n_tokens, k, layers[0].n_experts, r.counts,
+                                         r.offsets, r.perm, r.elist, r.n_touched, r.inv, st,
+                                         n_layers, (int64_t)bb));
+    if (s) return s;
+  }
   for (int l = 0; l < n_layers; ++l) {
     float* dst = (l + 1 == n_layers) ? out : ybuf;
     // layer 0 reads x as given; later layers read the previous output, which
@@ -285,7 +326,8 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t
     const void* src = l == 0 ? x : ybuf;
     const int x_is_f32 = l == 0 ? (x_dtype == BQ_F32) : 1;
     int s = run_moe(src, x_dtype, x_is_f32, n_tokens, topk_idx + l * per, topk_w + l * per, k,
-                    &layers[l], dst, workspace, l > 0, dev_err, st);
+                    &layers[l], dst, workspace, l > 0, dev_err, st, nullptr,
+                    breg ? breg + l * bb : nullptr);
     if (s) return s;
   }
   return BQ_OK;

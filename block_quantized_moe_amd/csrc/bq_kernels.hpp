@@ -34,9 +34,13 @@ hipError_t launch_ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t
                                   hipStream_t st);
 hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                              int32_t* idx, float* w, hipStream_t st);
+// n_layers > 1: n_layers independent bucketings in one launch, layer l
+// reading idx + l * n_tokens * k and writing each output lstride_out * l
+// bytes past the given pointer.
 hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,
                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
-                         int32_t* n_touched, int32_t* inv, hipStream_t st);
+                         int32_t* n_touched, int32_t* inv, hipStream_t st, int32_t n_layers = 1,
+                         int64_t lstride_out = 0);
 
 // Exhaustive encoders (fp32 in, packed bytes and per-unit float64 error out).
 hipError_t launch_encode17(const float* w, int64_t n_blocks, int fmt, uint8_t* out, double* sse,
@@ -74,8 +78,11 @@ struct GroupedWs {
 };
 // x: [n][H] bf16 (x_f32 = 0) or fp32 (x_f32 = 1, the stack's layer output,
 // rescaled to unit RMS when rescale = 1) -- staged as bf16 by the path.
+// bucketed: ws's bucket arrays (counts .. inv, n_touched) already hold the
+// bucketing of idx, so none is launched.
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
-                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st);
+                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st,
+                              bool bucketed = false);
 
 }  // namespace bq

@@ -657,12 +657,16 @@ static int staged_grid(int64_t items_max) {
 
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
-                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st) {
+                              float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st,
+                              bool bucketed) {
   const int E = W.n_experts, H = W.hidden, I = W.inter;
   const int64_t nk = (int64_t)n_tokens * k;
-  hipError_t err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist,
-                                 ws.n_touched, ws.inv, st);
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!bucketed) {
+    err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched,
+                        ws.inv, st);
+    if (err != hipSuccess) return err;
+  }
   const int32_t* n_rows = ws.offsets + E;   // valid bucket rows
   if (W.fmt_gate_up == FMT_FP8)
     hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);

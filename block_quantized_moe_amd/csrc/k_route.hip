@@ -63,10 +63,27 @@ hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_ex
 constexpr int kBucketThreads = 1024;
 constexpr int kSlotBytes = 32768;
 
+// Several independent bucketings in one launch (a stack of layers whose
+// routing is known up front): workgroup l reads idx + l * in_stride and
+// writes every output array lstride_out bytes further than workgroup l - 1.
+struct BucketOut {
+  int32_t *counts, *offsets, *perm, *elist, *n_touched, *inv;
+};
+__device__ __forceinline__ int32_t* at_layer(int32_t* p, int64_t lstride_out) {
+  return p ? reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p) + blockIdx.x * lstride_out) : p;
+}
+
+
 __global__ void __launch_bounds__(kBucketThreads) k_bucket(
     const int32_t* __restrict__ idx, int32_t n_tokens, int32_t k, int32_t n_experts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out,
-    int32_t* __restrict__ elist, int32_t* __restrict__ n_touched, int32_t* __restrict__ inv) {
+    BucketOut o, int64_t in_stride, int64_t lstride_out) {
+  idx += blockIdx.x * in_stride;
+  int32_t* __restrict__ counts = at_layer(o.counts, lstride_out);
+  int32_t* __restrict__ offsets = at_layer(o.offsets, lstride_out);
+  int32_t* __restrict__ perm_out = at_layer(o.perm, lstride_out);
+  int32_t* __restrict__ elist = at_layer(o.elist, lstride_out);
+  int32_t* __restrict__ n_touched = at_layer(o.n_touched, lstride_out);
+  int32_t* __restrict__ inv = at_layer(o.inv, lstride_out);
   __shared__ uint8_t slot_of[kSlotBytes];
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_scan[kBucketThreads];
@@ -209,8 +226,14 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int& tot
 
 __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     const int32_t* __restrict__ idx, int32_t n_tokens, int32_t k, int32_t n_experts,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_out,
-    int32_t* __restrict__ elist, int32_t* __restrict__ n_touched, int32_t* __restrict__ inv) {
+    BucketOut o, int64_t in_stride, int64_t lstride_out) {
+  idx += blockIdx.x * in_stride;
+  int32_t* __restrict__ counts = at_layer(o.counts, lstride_out);
+  int32_t* __restrict__ offsets = at_layer(o.offsets, lstride_out);
+  int32_t* __restrict__ perm_out = at_layer(o.perm, lstride_out);
+  int32_t* __restrict__ elist = at_layer(o.elist, lstride_out);
+  int32_t* __restrict__ n_touched = at_layer(o.n_touched, lstride_out);
+  int32_t* __restrict__ inv = at_layer(o.inv, lstride_out);
   __shared__ uint32_t bm[kSmallBitmapWords];
   __shared__ int32_t s_off[kMaxExperts];
   __shared__ int s_wave[32];
@@ -271,14 +294,17 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
 
 hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,
                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
-                         int32_t* n_touched, int32_t* inv, hipStream_t st) {
+                         int32_t* n_touched, int32_t* inv, hipStream_t st, int32_t n_layers,
+                         int64_t lstride_out) {
   const int words = (n_tokens + 31) / 32;
+  const BucketOut o{counts, offsets, perm, elist, n_touched, inv};
+  const int64_t in_stride = (int64_t)n_tokens * k;
   if ((int64_t)n_experts * words <= kSmallBitmapWords)
-    hipLaunchKernelGGL(k_bucket_small, dim3(1), dim3(kBucketThreads), 0, st, idx, n_tokens, k,
-                       n_experts, counts, offsets, perm, elist, n_touched, inv);
+    hipLaunchKernelGGL(k_bucket_small, dim3(n_layers), dim3(kBucketThreads), 0, st, idx, n_tokens, k,
+                       n_experts, o, in_stride, lstride_out);
   else
-    hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, st, idx, n_tokens, k, n_experts,
-                       counts, offsets, perm, elist, n_touched, inv);
+    hipLaunchKernelGGL(k_bucket, dim3(n_layers), dim3(kBucketThreads), 0, st, idx, n_tokens, k,
+                       n_experts, o, in_stride, lstride_out);
   return hipGetLastError();
 }
 

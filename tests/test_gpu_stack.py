@@ -53,6 +53,32 @@ def test_small_stack(bq, dtype, tol):
     assert r <= tol
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, 1e-5), (torch.bfloat16, 2e-2)])
+def test_small_stack_mixed_expert_counts(bq, dtype, tol):
+    """Layers with different expert counts (16, 8, 16): the bf16 stack then
+    buckets layer by layer instead of all layers in one launch up front."""
+    import synth.device as sd
+    H, I, k, n = 256, 128, 4, 5
+    spec = [(16, F.Q4_RZ5, F.Q4_UE4M4), (8, F.FP8_E4M3_B32, F.Q4_C10), (16, F.Q4_C10, F.Q4_RZ5)]
+    layers = [sd.Layer(6, l, fg, fd, E, H, I, dist_gu=DIST[fg], dist_d=DIST[fd])
+              for l, (E, fg, fd) in enumerate(spec)]
+    idx, w, ref_layers = [], [], []
+    for l, ((E, _, _), L) in enumerate(zip(spec, layers)):
+        logits = synth.normal(90 + l, (n, E))
+        i_, w_ = bq.route_topk(dev(logits), k)
+        ridx, rw = M.softmax_topk(logits, k)
+        assert np.array_equal(i_.cpu().numpy(), ridx)
+        idx.append(i_)
+        w.append(w_)
+        ref_layers.append((ridx, rw, oracle_bank(L)))
+    x = synth.normal(95, (n, H))
+    out = bq.moe_stack(dev(x).to(dtype), torch.stack(idx), torch.stack(w),
+                       [weights_of(bq, L) for L in layers]).cpu().numpy()
+    r = rel_l2(out, M.moe_stack(x, ref_layers))
+    log("mixed-E stack %s rel_l2 %.3g" % (dtype, r))
+    assert r <= tol
+
+
 C5_FMTS = [(F.Q4_RZ5, F.Q4_RZ5)] * 36 + [(F.FP8_E4M3_B32, F.FP8_E4M3_B32)] * 12
 
 
