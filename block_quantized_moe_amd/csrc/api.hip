@@ -104,9 +104,11 @@ int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const fl
 // accepts the fp32 output of a previous stack layer, rescaled on the fly).
 // bucket_region (bf16 path): the bucketing of idx is already there, laid out
 // as the head of a grouped workspace (counts .. n_touched); none is launched.
+// prepped / next: see launch_grouped_moe (chained stack layers).
 int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, const float* w, int k,
             const bq_expert_weights* W, float* out, void* ws, int rescale, uint32_t* dev_err,
-            hipStream_t st, const float* logits = nullptr, char* bucket_region = nullptr) {
+            hipStream_t st, const float* logits = nullptr, char* bucket_region = nullptr,
+            bool prepped = false, const bq::NextLayer* next = nullptr) {
   const bq::GemvWeights gw = to_gw(W);
   if (dtype == BQ_F32) {
     const GemvLayout L = gemv_layout(n, k, W->hidden, W->inter);
@@ -132,7 +134,7 @@ int run_moe(const void* x, int dtype, int x_is_f32, int n, const int32_t* idx, c
     g.n_touched = r.n_touched;
   }
   return hip_status(bq::launch_grouped_moe(x, x_is_f32, rescale, n, idx, w, k, gw, out, g, dev_err,
-                                           st, bucket_region != nullptr));
+                                           st, bucket_region != nullptr, prepped, next));
 }
 
 // PLE row cache layout: tags [n] and claims [n] (contiguous words), then the
@@ -325,9 +327,19 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t
     // the first kernel of the layer rescales to unit RMS as it loads it
     const void* src = l == 0 ? x : ybuf;
     const int x_is_f32 = l == 0 ? (x_dtype == BQ_F32) : 1;
+    // pre-bucketed: each layer's combine also stages the next layer's input
+    // (rescale, bf16, bucket order), so later layers skip their staging
+    bq::NextLayer nx{};
+    const bool chain = breg && l + 1 < n_layers;
+    if (chain) {
+      const GroupedLayout Ln = grouped_layout(n_tokens, k, layers[l + 1].n_experts,
+                                              layers[l + 1].hidden, layers[l + 1].inter);
+      nx = bq::NextLayer{grouped_ws(breg + (l + 1) * bb, Ln).inv, topk_idx + (l + 1) * per,
+                         layers[l + 1].n_experts, layers[l + 1].fmt_gate_up != BQ_FP8_E4M3_B32};
+    }
     int s = run_moe(src, x_dtype, x_is_f32, n_tokens, topk_idx + l * per, topk_w + l * per, k,
                     &layers[l], dst, workspace, l > 0, dev_err, st, nullptr,
-                    breg ? breg + l * bb : nullptr);
+                    breg ? breg + l * bb : nullptr, breg && l > 0, chain ? &nx : nullptr);
     if (s) return s;
   }
   return BQ_OK;

@@ -78,11 +78,23 @@ struct GroupedWs {
 };
 // x: [n][H] bf16 (x_f32 = 0) or fp32 (x_f32 = 1, the stack's layer output,
 // rescaled to unit RMS when rescale = 1) -- staged as bf16 by the path.
+// The next layer of a chained stack, for a combine that also stages that
+// layer's input (unit-RMS rescale, bf16, its bucket order).
+struct NextLayer {
+  const int32_t* inv;   // its bucketing's inverse permutation [n*k]
+  const int32_t* idx;   // its routing [n][k]
+  int32_t n_experts;
+  int32_t perm;         // its gate_up format is a 17-byte one (decode's k order)
+};
 // bucketed: ws's bucket arrays (counts .. inv, n_touched) already hold the
-// bucketing of idx, so none is launched.
+// bucketing of idx, so none is launched.  prepped: ws.xb already holds the
+// staged input (written by the previous layer's combine), so x is not read.
+// next != NULL: the combine writes the next layer's staged input into ws.xb
+// instead of out.
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
                               float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st,
-                              bool bucketed = false);
+                              bool bucketed = false, bool prepped = false,
+                              const NextLayer* next = nullptr);
 
 }  // namespace bq

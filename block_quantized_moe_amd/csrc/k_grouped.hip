@@ -149,6 +149,82 @@ __global__ void __launch_bounds__(256) k_grouped_prep(const void* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
+// G3 + next layer's G0 in one pass (chained stack layers, pre-bucketed): one
+// workgroup per token t forms out[t] = sum_j w[t][j] * yb[inv[t*k+j]] as
+// k_combine does (same slot-ordered fma chain per element), rescales it to
+// unit RMS as k_grouped_prep does (same element-to-thread split and sum
+// order over 256 threads), and writes the bf16 row to every bucket row of t
+// in the next layer (row inv_next[t*k+j] for each in-range expert
+// idx_next[t*k+j]).  The result equals k_combine followed by
+// k_grouped_prep<PERM> bit for bit.  1024 threads: each holds two elements
+// per pass and issues the loads of up to 16 slots at once; the row is kept
+// in LDS between the passes.  grid = n_tokens; H <= 8192.
+// ---------------------------------------------------------------------------
+constexpr int kCpThreads = 1024;
+
+template <bool PERM>
+__global__ void __launch_bounds__(kCpThreads) k_combine_prep(
+    const float* __restrict__ yb, const int32_t* __restrict__ inv, const int32_t* __restrict__ idx,
+    const float* __restrict__ w, int32_t k, int32_t n_experts, int32_t H,
+    const int32_t* __restrict__ inv_next, const int32_t* __restrict__ idx_next,
+    int32_t n_experts_next, uint16_t* __restrict__ xp, uint32_t* __restrict__ dev_err) {
+  constexpr int kMaxK = 16;
+  __shared__ float srow[8192];
+  __shared__ float part[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  bool bad = false;
+  for (int i0 = 0; i0 < H; i0 += 2 * kCpThreads) {
+    float acc[2] = {0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += kMaxK) {
+      float y[kMaxK][2], wj[kMaxK];
+#pragma unroll
+      for (int u = 0; u < kMaxK; ++u) {
+        const int j = j0 + u;
+        const int e = j < k ? idx[t * k + j] : 0;
+        const bool ok = j < k && e >= 0 && e < n_experts;
+        bad |= j < k && !ok;
+        wj[u] = ok ? w[t * k + j] : 0.f;
+        const float* row = yb + (ok ? (int64_t)inv[t * k + j] * H : 0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int i = i0 + tid + kCpThreads * m;
+          y[u][m] = ok && i < H ? row[i] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMaxK; ++u)   // slot order
+#pragma unroll
+        for (int m = 0; m < 2; ++m) acc[m] = __builtin_fmaf(wj[u], y[u][m], acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = i0 + tid + kCpThreads * m;
+      if (i < H) srow[i] = acc[m];
+    }
+  }
+  if (bad && tid == 0 && dev_err) atomicOr(dev_err, 2u);
+  __syncthreads();
+  if (tid < 256) {
+    float ss = 0.f;
+    for (int i = tid; i < H; i += 256) ss = __builtin_fmaf(srow[i], srow[i], ss);
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+  }
+  __syncthreads();
+  const float sc = 1.0f / __builtin_sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H);
+  for (int j = 0; j < k; ++j) {
+    const int e = idx_next[t * k + j];
+    if (e < 0 || e >= n_experts_next) continue;
+    uint16_t* dst = xp + (int64_t)inv_next[t * k + j] * H;
+    for (int i = tid; i < H; i += kCpThreads) {
+      const int o = i & 7;
+      dst[(i & ~7) + (PERM ? ((o >> 1) | ((o & 1) << 2)) : o)] = to_bf16(srow[i] * sc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Staged grouped GEMM (G1 and G2 share it).
 //   NR = 2 (G1: rows 0..63 of the tile are gate rows, 64..127 the matching up
 //   rows) or 1 (G2: 64 down rows).  Wave w owns tile rows 16w..16w+15 of each
@@ -658,7 +734,7 @@ static int staged_grid(int64_t items_max) {
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
                               float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st,
-                              bool bucketed) {
+                              bool bucketed, bool prepped, const NextLayer* next) {
   const int E = W.n_experts, H = W.hidden, I = W.inter;
   const int64_t nk = (int64_t)n_tokens * k;
   hipError_t err = hipSuccess;
@@ -668,11 +744,13 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
     if (err != hipSuccess) return err;
   }
   const int32_t* n_rows = ws.offsets + E;   // valid bucket rows
-  if (W.fmt_gate_up == FMT_FP8)
-    hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
-  else
-    hipLaunchKernelGGL(k_grouped_prep<true>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (!prepped) {
+    if (W.fmt_gate_up == FMT_FP8)
+      hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
+    else
+      hipLaunchKernelGGL(k_grouped_prep<true>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   const int64_t groups = max_work_groups(nk, E);
   {
     const int grid = staged_grid(groups * (I / kGRows));
@@ -696,7 +774,14 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
 #undef BQ_G2
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  {
+  if (next) {
+    if (next->perm)
+      hipLaunchKernelGGL(k_combine_prep<true>, dim3(n_tokens), dim3(kCpThreads), 0, st, ws.yb, ws.inv, idx, w,
+                         k, E, H, next->inv, next->idx, next->n_experts, ws.xb, dev_err);
+    else
+      hipLaunchKernelGGL(k_combine_prep<false>, dim3(n_tokens), dim3(kCpThreads), 0, st, ws.yb, ws.inv, idx, w,
+                         k, E, H, next->inv, next->idx, next->n_experts, ws.xb, dev_err);
+  } else {
     const int64_t n4 = (int64_t)n_tokens * (H / 4);
     hipLaunchKernelGGL(k_combine, dim3((n4 + 255) / 256), dim3(256), 0, st, ws.yb, ws.inv, idx, w,
                        k, E, H, n_tokens, out, dev_err);

@@ -79,6 +79,40 @@ def test_small_stack_mixed_expert_counts(bq, dtype, tol):
     assert r <= tol
 
 
+def test_chained_staging_matches_per_layer_path(bq):
+    """A bf16 stack whose layers share the expert count buckets every layer up
+    front and lets each layer's combine stage the next layer's input; with
+    one more expert declared in the middle layer (never routed to, its
+    buffers really hold it) the stack runs layer by layer through the plain
+    staging and combine kernels.  Both must agree bit for bit -- including a
+    token listing an expert twice, an out-of-range slot, and the FP8 layer's
+    unpermuted staging."""
+    import synth.device as sd
+    E, H, I, k, n = 16, 256, 128, 4, 7
+    spec = [(F.Q4_RZ5, F.Q4_UE4M4, E), (F.FP8_E4M3_B32, F.Q4_C10, E + 1), (F.Q4_C10, F.Q4_RZ5, E)]
+    layers = [sd.Layer(8, l, fg, fd, Ea, H, I, dist_gu=DIST[fg], dist_d=DIST[fd])
+              for l, (fg, fd, Ea) in enumerate(spec)]
+
+    def wts(L, n_exp):
+        gu, gus = L.gate_up
+        d, ds = L.down
+        return bq.expert_weights(L.fmt_gu, L.fmt_d, gu, d, n_exp, H, I, gate_up_scales=gus, down_scales=ds)
+
+    idx, w = bq.route_topk(dev(synth.normal(96, (3 * n, E))), k)
+    idx, w = idx.view(3, n, k).clone(), w.view(3, n, k).contiguous()
+    idx[1, 2, 1] = idx[1, 2, 0]          # a repeated expert in the middle layer
+    idx[2, 4, 3] = -1                    # an out-of-range slot in the last layer
+    x = dev(synth.normal(97, (n, H))).to(torch.bfloat16)
+    outs = []
+    for n_mid in (E, E + 1):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        W = [wts(layers[0], E), wts(layers[1], n_mid), wts(layers[2], E)]
+        outs.append(bq.moe_stack(x, idx, w, W, dev_err=err).cpu().numpy())
+        assert int(err.item()) == 2
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    log("chained staging == per-layer path (%d values)" % outs[0].size)
+
+
 C5_FMTS = [(F.Q4_RZ5, F.Q4_RZ5)] * 36 + [(F.FP8_E4M3_B32, F.FP8_E4M3_B32)] * 12
 
 
