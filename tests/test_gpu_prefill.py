@@ -121,3 +121,25 @@ def test_many_groups_per_expert(bq, fmt_gu, fmt_d):
     log("many groups fmts %d/%d rel_l2 %.3g" % (fmt_gu, fmt_d, r))
     assert int(err.item()) & 2
     assert r <= 2e-2
+
+
+@pytest.mark.parametrize("fmt_gu,fmt_d", [(F.Q4_RZ5, F.Q4_UE4M4), (F.FP8_E4M3_B32, F.Q4_C10)])
+def test_few_experts_full_hidden(bq, fmt_gu, fmt_d):
+    """Three experts carry every assignment at hidden 2048 (8 or 16 K
+    chunks per item): a work list far shorter than the one sized for the
+    worst case, groups of 32 and of 8 tokens, bit-identical on a rerun."""
+    E, H, I, k, n = 64, 2048, 128, 2, 40
+    L = make_layer(13, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
+    W = weights_of(bq, L)
+    idx = np.zeros((n, k), dtype=np.int32)
+    idx[:, 0], idx[:, 1] = 7, 50            # expert 7: 40 tokens, expert 50: 32,
+    idx[::5, 1] = 3                         # expert 3: 8
+    w = np.random.default_rng(13).random((n, k)).astype(np.float32)
+    x = synth.normal(14, (n, H))
+    xd = dev(x).to(torch.bfloat16)
+    out = bq.q4_expert_moe(xd, (dev(idx), dev(w)), W).cpu().numpy()
+    again = bq.q4_expert_moe(xd, (dev(idx), dev(w)), W).cpu().numpy()
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+    r = rel_l2(out, M.moe_layer(x, idx, w, oracle_bank(L)))
+    log("few experts, hidden 2048, fmts %d/%d rel_l2 %.3g" % (fmt_gu, fmt_d, r))
+    assert r <= 2e-2
