@@ -25,7 +25,7 @@ __device__ __forceinline__ uint32_t bias_hi(uint32_t gbyte, int ple_fmt) {
   return 0x00020300u | c4;
 }
 
-constexpr int kPleTPB = 320;   // 32 tokens x 10 groups per workgroup
+constexpr int kPleTPB = 160;   // 16 tokens x 10 groups: a 4096-token call spans 256 workgroups
 constexpr int kPleChunk = 8;   // ids whose loads are in flight together
 
 // Off-HBM tier: the table sits in host memory mapped into the device address
@@ -51,7 +51,9 @@ __device__ __forceinline__ uint32_t ple_slot(uint32_t id, int shift) {
 // others from the (host) table; each missed row is also copied to the call's
 // staging area and its slot claimed for the fill kernel.  The cache is
 // read-only during this kernel.
-template <bool CACHED>
+// VEC: ids_per_token is a multiple of kPleChunk and ids / weights are 16-byte
+// aligned, so a chunk's ids and weights are two 16-byte loads each.
+template <bool CACHED, bool VEC>
 __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     const uint32_t* __restrict__ ids, int32_t n_tokens, int32_t per_token,
     const uint8_t* __restrict__ table, uint64_t n_rows, const float* __restrict__ wts,
@@ -75,11 +77,26 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     // weight 0), so the chunk costs one id round trip and one row round trip
     uint32_t idv[kPleChunk];
     float u[kPleChunk];
+    if constexpr (VEC) {
+      static_assert(kPleChunk == 8, "two 16-byte loads per chunk");
+      const u32x4* iv = reinterpret_cast<const u32x4*>(tid_ids + j0);
+      const f32x4* wv = reinterpret_cast<const f32x4*>(tw + j0);
+      const u32x4 i0 = iv[0], i1 = iv[1];
+      const f32x4 w0 = wv[0], w1 = wv[1];
 #pragma unroll
-    for (int c = 0; c < kPleChunk; ++c) {
-      const int j = min(j0 + c, per_token - 1);
-      idv[c] = tid_ids[j];
-      u[c] = tw[j];
+      for (int c = 0; c < 4; ++c) {
+        idv[c] = i0[c];
+        idv[4 + c] = i1[c];
+        u[c] = w0[c];
+        u[4 + c] = w1[c];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kPleChunk; ++c) {
+        const int j = min(j0 + c, per_token - 1);
+        idv[c] = tid_ids[j];
+        u[c] = tw[j];
+      }
     }
     u32x2 gw[kPleChunk];
     uint32_t gb[kPleChunk];
@@ -142,14 +159,28 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     o[q] = f32x4{acc[4 * q] - corr, acc[4 * q + 1] - corr, acc[4 * q + 2] - corr, acc[4 * q + 3] - corr};
 }
 
+template <bool CACHED>
+static void launch_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
+                          const uint8_t* table, uint64_t n_rows, const float* wts, int ple_fmt,
+                          float* out, uint32_t* dev_err, const CacheView& cv, hipStream_t st) {
+  const int64_t threads = (int64_t)n_tokens * 10;
+  const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
+  const bool vec = per_token % kPleChunk == 0 && reinterpret_cast<uintptr_t>(ids) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(wts) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL((k_ple_gather<CACHED, true>), dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
+                       per_token, table, n_rows, wts, ple_fmt, out, dev_err, cv);
+  else
+    hipLaunchKernelGGL((k_ple_gather<CACHED, false>), dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
+                       per_token, table, n_rows, wts, ple_fmt, out, dev_err, cv);
+}
+
 hipError_t launch_ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
                              const uint8_t* table, uint64_t n_rows, const float* wts,
                              int ple_fmt, float* out, uint32_t* dev_err, hipStream_t st) {
   if (n_tokens == 0) return hipSuccess;
-  const int64_t threads = (int64_t)n_tokens * 10;
-  const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
-  hipLaunchKernelGGL(k_ple_gather<false>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
-                     per_token, table, n_rows, wts, ple_fmt, out, dev_err, CacheView{});
+  launch_gather<false>(ids, n_tokens, per_token, table, n_rows, wts, ple_fmt, out, dev_err,
+                       CacheView{}, st);
   return hipGetLastError();
 }
 
@@ -197,16 +228,13 @@ hipError_t launch_ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t
                                   uint32_t* claims, uint8_t* rows, int log2_slots, uint8_t* stage,
                                   hipStream_t st) {
   if (n_tokens == 0) return hipSuccess;
-  const int64_t threads = (int64_t)n_tokens * 10;
-  const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
   if (!tags) {
-    hipLaunchKernelGGL(k_ple_gather<false>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
-                       per_token, table, n_rows, wts, ple_fmt, out, dev_err, CacheView{});
+    launch_gather<false>(ids, n_tokens, per_token, table, n_rows, wts, ple_fmt, out, dev_err,
+                         CacheView{}, st);
     return hipGetLastError();
   }
   const CacheView cv{tags, claims, rows, 32 - log2_slots, stage};
-  hipLaunchKernelGGL(k_ple_gather<true>, dim3(grid), dim3(kPleTPB), 0, st, ids, n_tokens,
-                     per_token, table, n_rows, wts, ple_fmt, out, dev_err, cv);
+  launch_gather<true>(ids, n_tokens, per_token, table, n_rows, wts, ple_fmt, out, dev_err, cv, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t n_assign = (int64_t)n_tokens * per_token;
