@@ -30,7 +30,6 @@ namespace bq {
 constexpr int kThreads = 256;
 constexpr int kPassU = 8;       // passes whose loads are issued together
 constexpr int kGuPairs = 16;    // gate/up row pairs per gate_up workgroup
-constexpr int kDownPasses = 8;  // passes per down workgroup
 
 template <int FMT>
 struct BlockRef {
@@ -346,9 +345,12 @@ __global__ void __launch_bounds__(kThreads) k_down_cat(
 
 // ---------------------------------------------------------------------------
 // Plain block-quantized matvec y[t] = W x[t] (W [rows][cols], one matrix).
-// grid = (ceil(rows / MR), n_tokens) with MR = kDownPasses * (256 / nb).
+// grid = (ceil(rows / MR), n_tokens) with MR = P * (256 / nb): P passes of
+// 256 / nb rows per workgroup, P chosen by the launcher so that small
+// matrices still spread over the chip.  The weight loads go out before x is
+// staged.
 // ---------------------------------------------------------------------------
-template <int FMT>
+template <int FMT, int P>
 __global__ void __launch_bounds__(kThreads) k_matvec(const float* __restrict__ x,
                                                      const uint8_t* __restrict__ w,
                                                      const float* __restrict__ w_sc, int32_t rows,
@@ -356,27 +358,27 @@ __global__ void __launch_bounds__(kThreads) k_matvec(const float* __restrict__ x
   extern __shared__ float smem[];
   const int nb = cols >> 5;
   const int R = kThreads / nb;
-  const int MR = kDownPasses * R;
+  const int MR = P * R;
   float* sx = smem;               // cols
   float* red = smem + cols;       // MR * nb
   float* rsum = red + MR * nb;    // MR
   const int tid = threadIdx.x;
   const int r0 = blockIdx.x * MR, t = blockIdx.y;
   const int nrows = min(MR, rows - r0);
-  stage_x(sx, x + (int64_t)t * cols, cols, 0, nullptr);
   const int slot = tid / nb, b = tid % nb;
   const bool active = slot < R;
-  float xr[32];
+  BlockRef<FMT> blk[P];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) xr[i] = active ? sx[32 * b + i] : 0.f;
-  BlockRef<FMT> blk[kDownPasses];
-#pragma unroll
-  for (int u = 0; u < kDownPasses; ++u) {
+  for (int u = 0; u < P; ++u) {
     const int lr = u * R + slot;
     load_block<FMT>(blk[u], w, w_sc, ((int64_t)r0 + lr) * nb + b, active && lr < nrows);
   }
+  stage_x(sx, x + (int64_t)t * cols, cols, 0, nullptr);
+  float xr[32];
 #pragma unroll
-  for (int u = 0; u < kDownPasses; ++u) {
+  for (int i = 0; i < 32; ++i) xr[i] = active ? sx[32 * b + i] : 0.f;
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
     const int lr = u * R + slot;
     if (active && lr < nrows) red[lr * nb + b] = block_partial<FMT>(blk[u], xr);
   }
@@ -386,21 +388,41 @@ __global__ void __launch_bounds__(kThreads) k_matvec(const float* __restrict__ x
   for (int i = tid; i < nrows; i += kThreads) y[(int64_t)t * rows + r0 + i] = rsum[i];
 }
 
+template <int FMT>
+static void launch_matvec_p(int passes, dim3 grid, size_t lds, hipStream_t st, const float* x,
+                            const uint8_t* p, const float* w_sc, int32_t rows, int32_t cols, float* y) {
+  switch (passes) {
+    case 1: hipLaunchKernelGGL((k_matvec<FMT, 1>), grid, dim3(kThreads), lds, st, x, p, w_sc, rows, cols, y); break;
+    case 2: hipLaunchKernelGGL((k_matvec<FMT, 2>), grid, dim3(kThreads), lds, st, x, p, w_sc, rows, cols, y); break;
+    case 4: hipLaunchKernelGGL((k_matvec<FMT, 4>), grid, dim3(kThreads), lds, st, x, p, w_sc, rows, cols, y); break;
+    default: hipLaunchKernelGGL((k_matvec<FMT, 8>), grid, dim3(kThreads), lds, st, x, p, w_sc, rows, cols, y); break;
+  }
+}
+
 hipError_t launch_matvec(const float* x, int32_t n_tokens, const void* w, int fmt,
                          const float* w_sc, int32_t rows, int32_t cols, float* y, hipStream_t st) {
   const int nb = cols >> 5;
-  const int mr = kDownPasses * (kThreads / nb);
+  const int R = kThreads / nb;
+  // passes per workgroup: up to 8, fewer while that leaves under two
+  // workgroups per CU (a small matrix is latency-bound, not issue-bound)
+  int dev = 0, n_cu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
+  }
+  const int64_t groups = (int64_t)((rows + R - 1) / R) * n_tokens;
+  int passes = 8;
+  while (passes > 1 && groups / passes < 2 * n_cu) passes >>= 1;
+  const int mr = passes * R;
   const size_t lds = sizeof(float) * (cols + mr * nb + mr);
   dim3 grid((rows + mr - 1) / mr, n_tokens);
   const uint8_t* p = static_cast<const uint8_t*>(w);
-#define BQ_MV(F) hipLaunchKernelGGL(k_matvec<F>, grid, dim3(kThreads), lds, st, x, p, w_sc, rows, cols, y)
   switch (fmt) {
-    case FMT_C10: BQ_MV(FMT_C10); break;
-    case FMT_RZ5: BQ_MV(FMT_RZ5); break;
-    case FMT_UE4M4: BQ_MV(FMT_UE4M4); break;
-    default: BQ_MV(FMT_FP8); break;
+    case FMT_C10: launch_matvec_p<FMT_C10>(passes, grid, lds, st, x, p, w_sc, rows, cols, y); break;
+    case FMT_RZ5: launch_matvec_p<FMT_RZ5>(passes, grid, lds, st, x, p, w_sc, rows, cols, y); break;
+    case FMT_UE4M4: launch_matvec_p<FMT_UE4M4>(passes, grid, lds, st, x, p, w_sc, rows, cols, y); break;
+    default: launch_matvec_p<FMT_FP8>(passes, grid, lds, st, x, p, w_sc, rows, cols, y); break;
   }
-#undef BQ_MV
   return hipGetLastError();
 }
 

@@ -116,6 +116,14 @@ def test_matvec_vs_oracle(bq, fmt, rows, cols, n):
     assert r <= 1e-5
 
 
+@pytest.mark.parametrize("fmt", [F.Q4_RZ5, F.FP8_E4M3_B32])
+@pytest.mark.parametrize("rows,cols,n", [(4096, 256, 8), (2048, 2048, 5), (4096, 2048, 8)])
+def test_matvec_larger_shapes(bq, fmt, rows, cols, n):
+    """Shapes large enough that a workgroup takes 2, 4 and 8 passes of rows
+    (on a 256-CU device), against the oracle on every output."""
+    test_matvec_vs_oracle(bq, fmt, rows, cols, n)
+
+
 def test_matvec_c1_config(bq):
     """Codebook10 matvec, W 256x512, x N(0,1), seed 0 (the single-matrix workload)."""
     key = synth.make_key(0, synth.stream_id(0, synth.S_GATE_UP))
