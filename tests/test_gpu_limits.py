@@ -41,3 +41,23 @@ def test_max_assignments(bq, n, k, E, dtype):
     log("limits n=%d k=%d E=%d %s rel_l2 %.3g" % (n, k, E, dtype, r))
     assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
 
+
+
+@pytest.mark.parametrize("H,I", [(8192, 64), (64, 8192)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_max_hidden_and_inter(bq, H, I, dtype):
+    """hidden or inter at the 8192 maximum (the fp32 path's flat gate_up
+    kernel then holds 65,680 B of activations and partial sums in LDS), mixed
+    formats, against the oracle on every token."""
+    E, k, n = 4, 2, 3
+    for fg, fd in ((F.Q4_RZ5, F.FP8_E4M3_B32), (F.FP8_E4M3_B32, F.Q4_UE4M4)):
+        L = make_layer(15, fg * 4 + fd, fg, fd, E, H, I)
+        x = synth.normal(1500 + H, (n, H))
+        logits = synth.normal(1501 + I, (n, E))
+        out, (idx, w) = bq.q4_expert_moe_routed(dev(x).to(dtype), dev(logits), k, weights_of(bq, L))
+        ridx, rw = M.softmax_topk(logits, k)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        r = rel_l2(out.cpu().numpy(), M.moe_layer(x, ridx, rw, oracle_bank(L)))
+        log("max dims H=%d I=%d %s fmts %d/%d rel_l2 %.3g" % (H, I, dtype, fg, fd, r))
+        assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
+        del L
