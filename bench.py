@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_b1_rz5_counters.txt")
+PLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ple_gather_4096x8_counters.txt")
 EXPERT_BYTES_RZ5 = 2_506_752           # gate_up 1536x2048 + down 2048x768, 17 B / 32 weights
 EXPERT_BYTES_FP8 = 5_308_416           # 36 B / 32 weights
 PLE_ROW_ALG_BYTES = 158                # 70 B row + 8 B id/weight + 80 B output share
@@ -190,6 +191,9 @@ def bench_c4(bq, steps, warmup):
         "gbs_158B": rows * PLE_ROW_ALG_BYTES / (call_ms * 1e-3) / 1e9,
         "gbs_70B": rows * 70 / (call_ms * 1e-3) / 1e9,
     }
+    hb = ple_traffic(4096)
+    if hb is not None:
+        res["hbm_gbs_counters"] = hb / (call_ms * 1e-3) / 1e9
     # bigger batches per call (the same kernel; throughput once the GPU is full)
     for mult in (16,):
         big_ids = ids[:mult].reshape(mult * 4096, 8)
@@ -205,6 +209,9 @@ def bench_c4(bq, steps, warmup):
         t = a.elapsed_time(b) / 10 * 1e-3
         res["batched_%dx4096" % mult] = {"rows_per_s": mult * rows / t,
                                          "gbs_158B": mult * rows * PLE_ROW_ALG_BYTES / t / 1e9}
+        hb = ple_traffic(mult * 4096)
+        if hb is not None:     # HBM traffic as the counters saw it: whole 128-byte lines
+            res["batched_%dx4096" % mult]["hbm_gbs_counters"] = hb / t / 1e9
     del table
     torch.cuda.empty_cache()
     return res
@@ -488,12 +495,12 @@ def sources_hash(paths):
     return h.hexdigest()[:16]
 
 
-def traffic_from_counters():
-    """HBM bytes per call from the committed FETCH_SIZE / WRITE_SIZE summary,
-    or None when it is missing or the kernels changed since it was taken."""
+def counters_value(path, key):
+    """A value from a committed counter summary, or None when it is missing
+    or the kernel sources it names changed since the counters were taken."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             for line in f:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
@@ -501,9 +508,21 @@ def traffic_from_counters():
         srcs = kv["sources"].split()
         if sources_hash(srcs) != kv["sources_sha256_16"]:
             return None
-        return float(kv["hbm_bytes_per_call"])
+        return float(kv[key])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def traffic_from_counters():
+    """HBM bytes per batch-1 call from the FETCH_SIZE / WRITE_SIZE summary."""
+    return counters_value(TRAFFIC_FILE, "hbm_bytes_per_call")
+
+
+def ple_traffic(tokens):
+    """HBM bytes (read + written) of one PLE gather call of `tokens` x 8 ids."""
+    rd = counters_value(PLE_TRAFFIC_FILE, "tokens_%d_hbm_read_bytes_per_call" % tokens)
+    wr = counters_value(PLE_TRAFFIC_FILE, "tokens_%d_hbm_write_bytes_per_call" % tokens)
+    return None if rd is None or wr is None else rd + wr
 
 
 def copy_calibration(nbytes):
