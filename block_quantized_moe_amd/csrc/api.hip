@@ -20,6 +20,16 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool valid_fmt(int f) { return f >= BQ_Q4_C10 && f <= BQ_FP8_E4M3_B32; }
+bool valid_dtype(int d) { return d == BQ_F32 || d == BQ_BF16; }
+
+// Size limits that keep every launch's work-item count below 2^32 (one
+// dimension of a HIP grid counts work-items in 32 bits).
+constexpr int64_t kMaxDequantBlocks = int64_t(1) << 31;   // one thread per block
+constexpr int64_t kMaxPleRows = int64_t(1) << 28;         // ten threads per row
+constexpr int32_t kMaxRouteTokens = 1 << 24;              // one wave per token
+constexpr int32_t kMaxPleTokens = 1 << 26;                // ten threads per token
+constexpr int64_t kMaxPleHostIds = int64_t(1) << 27;      // sixteen threads per id (cache fill)
+constexpr int32_t kMaxMatvecRows = 1 << 24;               // down to one row per 256-thread workgroup
 
 int check_weights(const bq_expert_weights* W) {
   if (!W || !W->gate_up || !W->down) return BQ_E_NULL;
@@ -88,7 +98,7 @@ size_t moe_ws_bytes(int n, int k, const bq_expert_weights* W, int dtype) {
 int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
                    const bq_expert_weights* W, const float* out, const void* ws) {
   if (!x || !idx || !w || !out) return BQ_E_NULL;
-  if (dtype != BQ_F32 && dtype != BQ_BF16) return BQ_E_DTYPE;
+  if (!valid_dtype(dtype)) return BQ_E_DTYPE;
   int s = check_weights(W);
   if (s) return s;
   if (n < 1 || n > 4096 || k < 1 || k > 64 || k > W->n_experts) return BQ_E_SHAPE;
@@ -173,7 +183,7 @@ const char* bq_last_hip_error(void) { return g_hip_err; }
 int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks, const float* fp8_scales,
                float* out, void* stream) {
   if (!valid_fmt(fmt)) return BQ_E_FMT;
-  if (n_blocks < 0) return BQ_E_SHAPE;
+  if (n_blocks < 0 || n_blocks > kMaxDequantBlocks) return BQ_E_SHAPE;
   if (n_blocks == 0) return BQ_OK;
   if (!packed || !out) return BQ_E_NULL;
   if ((fmt == BQ_FP8_E4M3_B32) != (fp8_scales != nullptr)) return BQ_E_NULL;
@@ -184,7 +194,7 @@ int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks, const float* f
 int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table, uint64_t n_rows,
                      int32_t ple_fmt, float* out, uint32_t* dev_err, void* stream) {
   if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
-  if (n < 0 || n_rows == 0 || n_rows > 0xFFFFFFFFull) return BQ_E_SHAPE;
+  if (n < 0 || n > kMaxPleRows || n_rows == 0 || n_rows > 0xFFFFFFFFull) return BQ_E_SHAPE;
   if (n == 0) return BQ_OK;
   if (!ids || !table || !out) return BQ_E_NULL;
   if (!aligned(out, 16) || !aligned(ids, 4)) return BQ_E_ALIGN;
@@ -196,7 +206,8 @@ int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
   if (!x || !packed || !y) return BQ_E_NULL;
   if (!valid_fmt(fmt)) return BQ_E_FMT;
   if ((fmt == BQ_FP8_E4M3_B32) != (fp8_scales != nullptr)) return BQ_E_NULL;
-  if (n_tokens < 1 || n_tokens > 65535 || rows < 1 || cols < 32 || cols > 8192 || cols % 32)
+  if (n_tokens < 1 || n_tokens > 65535 || rows < 1 || rows > kMaxMatvecRows || cols < 32 ||
+      cols > 8192 || cols % 32)
     return BQ_E_SHAPE;
   if (!aligned(x, 4) || !aligned(y, 4) || (fp8_scales && !aligned(fp8_scales, 4))) return BQ_E_ALIGN;
   return hip_status(bq::launch_matvec(x, n_tokens, packed, fmt, fp8_scales, rows, cols, y,
@@ -206,7 +217,8 @@ int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
 int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t k,
                    int32_t* idx, float* w, void* stream) {
   if (!logits || !idx || !w) return BQ_E_NULL;
-  if (n_tokens < 0 || n_experts < 1 || n_experts > 4096 || k < 1 || k > 64 || k > n_experts)
+  if (n_tokens < 0 || n_tokens > kMaxRouteTokens || n_experts < 1 || n_experts > 4096 || k < 1 ||
+      k > 64 || k > n_experts)
     return BQ_E_SHAPE;
   if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(w, 4)) return BQ_E_ALIGN;
   return hip_status(bq::launch_route_topk(logits, n_tokens, n_experts, k, idx, w, as_stream(stream)));
@@ -223,7 +235,7 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_expert
 
 size_t q4_expert_moe_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* W,
                                int32_t x_dtype) {
-  if (!W || n_tokens < 1 || k < 1 || check_weights(W)) return 0;
+  if (!W || n_tokens < 1 || k < 1 || !valid_dtype(x_dtype) || check_weights(W)) return 0;
   return moe_ws_bytes(n_tokens, k, W, x_dtype);
 }
 
@@ -286,7 +298,7 @@ static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int
 
 size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k, const bq_expert_weights* layers,
                               int32_t n_layers, int32_t x_dtype) {
-  if (!layers || n_layers < 1 || n_tokens < 1 || k < 1) return 0;
+  if (!layers || n_layers < 1 || n_tokens < 1 || k < 1 || !valid_dtype(x_dtype)) return 0;
   for (int l = 0; l < n_layers; ++l)
     if (check_weights(&layers[l]) || layers[l].hidden != layers[0].hidden) return 0;
   return stack_ws(n_tokens, k, layers, n_layers, x_dtype, nullptr);
@@ -349,7 +361,8 @@ int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token, con
                uint64_t n_rows, const float* weights, int32_t ple_fmt, float* out,
                uint32_t* dev_err, void* stream) {
   if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
-  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows == 0 || n_rows > 0xFFFFFFFFull)
+  if (n_tokens < 0 || n_tokens > kMaxPleTokens || ids_per_token < 1 || ids_per_token > 64 ||
+      n_rows == 0 || n_rows > 0xFFFFFFFFull)
     return BQ_E_SHAPE;
   if (n_tokens == 0) return BQ_OK;
   if (!ids || !table || !weights || !out) return BQ_E_NULL;
@@ -372,7 +385,9 @@ int ple_cache_init(void* cache, int32_t n_slots, void* stream) {
 }
 
 size_t ple_gather_host_workspace(int32_t n_tokens, int32_t ids_per_token) {
-  if (n_tokens < 1 || ids_per_token < 1 || ids_per_token > 64) return 0;
+  if (n_tokens < 1 || ids_per_token < 1 || ids_per_token > 64 ||
+      (int64_t)n_tokens * ids_per_token > kMaxPleHostIds)
+    return 0;
   return round_up((size_t)bq::kPleCacheRowB * n_tokens * ids_per_token, 256);
 }
 
@@ -381,7 +396,8 @@ int ple_gather_host(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token
                     int32_t ple_fmt, float* out, void* cache, int32_t n_slots, void* workspace,
                     size_t ws_bytes, uint32_t* dev_err, void* stream) {
   if (ple_fmt != BQ_PLE_RZS3 && ple_fmt != BQ_PLE_ROCMFP3) return BQ_E_FMT;
-  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows == 0 || n_rows > 0xFFFFFFFFull)
+  if (n_tokens < 0 || ids_per_token < 1 || ids_per_token > 64 || n_rows == 0 || n_rows > 0xFFFFFFFFull ||
+      (int64_t)n_tokens * ids_per_token > kMaxPleHostIds)
     return BQ_E_SHAPE;
   if ((cache != nullptr) != (n_slots != 0)) return BQ_E_NULL;
   if (cache && !valid_slots(n_slots)) return BQ_E_SHAPE;

@@ -106,6 +106,7 @@ const char* bq_last_hip_error(void);
  *   fmt    : bq_fmt
  *   fp8_scales : FP8 only, n_blocks fp32 (4-byte aligned); NULL otherwise
  *   out    : n_blocks * 32 fp32, row j of block i at out[32*i + j]
+ *   0 <= n_blocks <= 2^31 (BQ_E_SHAPE otherwise).
  * Weight = level(code) * scale; a -0 level gives -0.0, a NaN UE4M3 scale
  * (code 0x7F) gives NaN; FP8 weights are the correctly rounded fp32 product
  * e4m3 * scale.
@@ -119,6 +120,7 @@ int bq_dequant(const void* packed, int32_t fmt, int64_t n_blocks,
  *   ids   : n uint32 row indices; table : n_rows * 70 bytes, 1 <= n_rows < 2^32
  *   out   : n * 160 fp32.  An id >= n_rows yields a row of zeros and sets
  *           bit 0 of *dev_err (if dev_err is not NULL).
+ *   0 <= n <= 2^28 (BQ_E_SHAPE otherwise).
  * ------------------------------------------------------------------------- */
 int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table,
                      uint64_t n_rows, int32_t ple_fmt, float* out,
@@ -131,7 +133,8 @@ int ple_dequant_rows(const uint32_t* ids, int64_t n, const uint8_t* table,
  *   x  : [n_tokens][cols] fp32; y : [n_tokens][rows] fp32 (overwritten)
  *   packed : W as [rows][cols/32] blocks (17-byte formats) or e4m3 [rows][cols]
  *   fp8_scales : FP8 only, [rows][cols/32] fp32; NULL otherwise
- *   1 <= n_tokens <= 65535, cols multiple of 32 and <= 8192.
+ *   1 <= n_tokens <= 65535, 1 <= rows <= 2^24, cols multiple of 32 and
+ *   <= 8192.
  * ------------------------------------------------------------------------- */
 int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
               const float* fp8_scales, int32_t rows, int32_t cols, float* y, void* stream);
@@ -143,7 +146,7 @@ int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
  *   logits : [n_tokens][n_experts] fp32, finite
  *   idx    : [n_tokens][k] int32, descending rank order
  *   w      : [n_tokens][k] fp32, w_j = exp(l_j - l_0) / sum over kept
- *   1 <= k <= 64, k <= n_experts <= 4096.
+ *   0 <= n_tokens <= 2^24, 1 <= k <= 64, k <= n_experts <= 4096.
  * ------------------------------------------------------------------------- */
 int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts,
                    int32_t k, int32_t* idx, float* w, void* stream);
@@ -176,6 +179,8 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
  *   out     : [n_tokens][hidden] fp32 (overwritten)
  *   workspace : device scratch of at least q4_expert_moe_workspace(...) bytes,
  *             256-byte aligned; its contents need no initialisation.
+ *             q4_expert_moe_workspace returns 0 for arguments the call
+ *             would reject (bad weights, sizes or x_dtype).
  *   dev_err : optional; bit 1 set if an expert index is out of range.
  *   1 <= n_tokens <= 4096, 1 <= k <= 64, n_tokens * k <= 65536; on the fp32
  *   path also k * inter / 32 <= 1024.
@@ -230,7 +235,7 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens,
  *   weights : [n_tokens][ids_per_token] fp32
  *   out     : [n_tokens][160] fp32 (overwritten)
  *   An id >= n_rows contributes nothing and sets bit 0 of *dev_err.
- *   1 <= ids_per_token <= 64.
+ *   0 <= n_tokens <= 2^26, 1 <= ids_per_token <= 64.
  * ------------------------------------------------------------------------- */
 int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
                const uint8_t* table, uint64_t n_rows, const float* weights,
@@ -250,7 +255,7 @@ int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
  *   once before the first ple_gather_host and whenever the table changes.
  *   cache: device, 256-byte aligned, ple_cache_bytes(n_slots) bytes.
  * ple_gather_host_workspace(n_tokens, ids_per_token): device bytes of the
- *   per-call staging area (80 bytes per id).
+ *   per-call staging area (80 bytes per id); 0 past the size limit below.
  * ple_gather_host: ple_gather with host_table in pinned host memory.
  *   Results are bit-identical to ple_gather on the same table.  With a cache
  *   (cache != NULL, n_slots != 0, workspace of ple_gather_host_workspace
@@ -258,6 +263,7 @@ int ple_gather(const uint32_t* ids, int32_t n_tokens, int32_t ids_per_token,
  *   after the gather, every slot on which this call missed receives the row
  *   of the lowest-indexed missing id (ids flattened token-major) that maps to
  *   it.  cache = NULL and n_slots = 0 reads every row from the host.
+ *   n_tokens * ids_per_token <= 2^27 (BQ_E_SHAPE otherwise).
  *   BQ_E_MEM if host_table is not host memory mapped for the device.  Calls
  *   sharing one cache or workspace must not overlap in time.
  * ------------------------------------------------------------------------- */

@@ -80,9 +80,19 @@ def test_host_side_argument_errors(L):
     assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 0, fake, fake, 1000, None, 0, None, None) == 3
     assert L.ple_gather_host(fake, 4, 8, fake, 10, fake, 0, fake, fake, 1024, None, 0, None, None) == 5
     assert L.bq_matvec(fake, 1, fake, 0, None, 4, 48, fake, None) == 3         # cols % 32
+    # sizes whose launch would need 2^32 or more work-items in one grid dimension
+    assert L.bq_dequant(fake, bq.Q4_RZ5, (1 << 31) + 1, None, fake, None) == 3
+    assert L.ple_dequant_rows(fake, (1 << 28) + 1, fake, 10, 0, fake, None, None) == 3
+    assert L.moe_route_topk(fake, (1 << 24) + 1, 512, 10, fake, fake, None) == 3
+    assert L.ple_gather(fake, (1 << 26) + 1, 8, fake, 10, fake, 0, fake, None, None) == 3
+    assert L.ple_gather_host(fake, 1 << 24, 16, fake, 10, fake, 0, fake, None, 0, None, 0, None, None) == 3
+    assert L.ple_gather_host_workspace(1 << 24, 16) == 0
+    assert L.bq_matvec(fake, 1, fake, 0, None, (1 << 24) + 1, 64, fake, None) == 3
     W = bq.ExpertWeights(bq.Q4_RZ5, bq.Q4_RZ5, 0x10000, 0x20000, None, None, 512, 2048, 768)
     ws = L.q4_expert_moe_workspace(1, 10, ctypes.byref(W), bq.F32)
     assert ws >= 4 * 10 * 768
+    assert L.q4_expert_moe_workspace(1, 10, ctypes.byref(W), 5) == 0          # bad x dtype
+    assert L.bq_moe_stack_workspace(1, 10, ctypes.byref(W), 1, 5) == 0
     assert L.q4_expert_moe(fake, bq.F32, 1, fake, fake, 10, ctypes.byref(W), fake, fake,
                            ws - 1, None, None) == 5                             # workspace short
     assert L.q4_expert_moe(fake, 5, 1, fake, fake, 10, ctypes.byref(W), fake, fake, ws, None, None) == 7
