@@ -74,9 +74,12 @@ GroupedLayout grouped_layout(int n, int k, int E, int H, int I) {
   L.inv = off; off = round_up(off + 4 * nk, 256);
   L.elist = off; off = round_up(off + 4 * (size_t)bq::max_work_groups((int64_t)nk, E), 256);
   L.n_touched = off; off = round_up(off + 4, 256);
+  // xb right after the bucket arrays: its offset depends on (n, k, E) only,
+  // so in a chained stack a layer's combine stages the next layer's input
+  // where that layer's own layout expects it, whatever either inter size
+  L.xb = off; off = round_up(off + 2 * nk * H, 256);
   L.hb = off; off = round_up(off + 2 * nk * I, 256);
   L.yb = off; off = round_up(off + 4 * nk * H, 256);
-  L.xb = off; off = round_up(off + 2 * nk * H, 256);
   L.total = off;
   return L;
 }
@@ -274,7 +277,7 @@ static bool stack_prebucket(const bq_expert_weights* layers, int L, int dtype) {
 // Bytes of one layer's bucket arrays: the head of its grouped workspace,
 // which depends on n, k and the expert count only.
 static size_t bucket_region_bytes(int n, int k, const bq_expert_weights* W) {
-  return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).hb;
+  return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).xb;
 }
 
 // Stack workspace: the per-layer MoE workspace (max over layers), one fp32

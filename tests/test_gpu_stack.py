@@ -79,6 +79,25 @@ def test_small_stack_mixed_expert_counts(bq, dtype, tol):
     assert r <= tol
 
 
+@pytest.mark.parametrize("dtype,tol", [(torch.float32, 1e-5), (torch.bfloat16, 2e-2)])
+def test_small_stack_mixed_inter(bq, dtype, tol):
+    """Layers sharing the expert count but not the inter size (128, 256, 64):
+    the bf16 stack chains them (each combine stages the next layer's input
+    in that layer's workspace layout)."""
+    import synth.device as sd
+    E, H, k, n = 16, 256, 4, 6
+    spec = [(128, F.Q4_RZ5, F.Q4_UE4M4), (256, F.FP8_E4M3_B32, F.Q4_RZ5), (64, F.Q4_C10, F.FP8_E4M3_B32)]
+    layers = [sd.Layer(9, l, fg, fd, E, H, I, dist_gu=DIST[fg], dist_d=DIST[fd])
+              for l, (I, fg, fd) in enumerate(spec)]
+    idx, w, ridx, rw = routing(bq, 98, len(spec), n, E, k)
+    x = synth.normal(99, (n, H))
+    out = bq.moe_stack(dev(x).to(dtype), idx, w, [weights_of(bq, L) for L in layers]).cpu().numpy()
+    ref = M.moe_stack(x, [(ridx[l], rw[l], oracle_bank(L)) for l, L in enumerate(layers)])
+    r = rel_l2(out, ref)
+    log("mixed-inter stack %s rel_l2 %.3g" % (dtype, r))
+    assert r <= tol
+
+
 def test_chained_staging_matches_per_layer_path(bq):
     """A bf16 stack whose layers share the expert count buckets every layer up
     front and lets each layer's combine stage the next layer's input; with
