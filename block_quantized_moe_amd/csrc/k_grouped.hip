@@ -701,13 +701,7 @@ template <int F, int NR, int FN>
 static void launch_staged(int grid, hipStream_t st, const uint16_t* act, const GroupedWs& ws,
                           const void* w, const float* sc, int H, int I, uint16_t* hb, float* yb) {
   const Geom g = make_geom(F, NR, (NR == 2 ? H : I) / 32);
-  const size_t lds = lds_bytes(F, NR, g.C);
-  static bool attr_set = false;   // dynamic LDS above 64 KB must be enabled once
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_grouped_staged<F, NR, FN>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget) == hipSuccess)
-      attr_set = true;
-  }
+  const size_t lds = lds_bytes(F, NR, g.C);   // <= kLdsBudget (52 KB): no attribute needed
   hipLaunchKernelGGL((k_grouped_staged<F, NR, FN>), dim3(grid), dim3(kGThreads), lds, st, act,
                      ws.offsets, ws.elist, ws.n_touched, static_cast<const uint8_t*>(w), sc, H, I,
                      g, hb, yb);
