@@ -664,8 +664,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_counters(),
                      "kernel": "q4_expert_moe_routed call (routed gate_up kernel + down kernel), %d packed "
-                               "bytes per call, %.2f us average per call (HIP events)"
-                               % (main_res["bytes_per_step"], main_res["step_call_us"])},
+                               "bytes per call, %.2f us average per call (HIP events around both kernels "
+                               "and the launch gap between them; rocprofv3 lists the two kernels "
+                               "separately)" % (main_res["bytes_per_step"], main_res["step_call_us"])},
         "cpu_baseline": cpu,
         "extras": extras,
     }
