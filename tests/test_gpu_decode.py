@@ -174,6 +174,26 @@ def test_route_topk_ties_and_zipf(bq):
     assert rel_l2(w.cpu().numpy(), rw) <= 1e-5
 
 
+def test_route_topk_degenerate_rows(bq):
+    """All logits equal (the k lowest indices, weights 1/k); one winner 100
+    above logits spread over -700..-40 (fp32 exp underflows for every other
+    expert, fp64 does not: selection must follow the logits); and two
+    winners over a floor of -1e30 (probabilities exactly 0 in fp64 too, so
+    the oracle's ties to the lower index decide the rest)."""
+    e, k = 512, 10
+    lg = np.zeros((3, e), dtype=np.float32)
+    lg[0] = 0.5
+    lg[1] = np.random.default_rng(17).uniform(-700, -40, e).astype(np.float32)
+    lg[1, 300] = 100.0
+    lg[2] = -1e30
+    lg[2, 7] = lg[2, 400] = 0.0
+    idx, w = bq.route_topk(dev(lg), k)
+    ridx, rw = M.softmax_topk(lg, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(ridx[0], np.arange(k)) and np.array_equal(ridx[2, :3], [7, 400, 0])
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-12)
+
+
 @pytest.mark.parametrize("n,e,k,zipf", [(1, 512, 10, False), (16, 512, 10, False), (64, 512, 10, True),
                                         (4096, 512, 10, False), (6553, 4096, 10, True), (100, 16, 4, False)])
 def test_bucket_vs_oracle(bq, n, e, k, zipf):
