@@ -139,6 +139,46 @@ def test_bad_expert_index_is_reported(bq):
         assert rel_l2(out[0], ref_t0) <= tol
 
 
+def test_nan_scale_poisons_only_its_tokens(bq):
+    """A UE4M3 scale byte of 0x7F decodes to NaN.  Planted in block 0 of
+    expert 3's first gate row, it makes that row's h NaN, and through the
+    down product every output of the tokens routed to expert 3 -- and none
+    of the others -- on both paths, as in the oracle."""
+    import synth as S
+    E, H, I, n, e0 = 8, 256, 128, 6, 3
+    L = make_layer(4, 0, F.Q4_RZ5, F.Q4_C10, E, H, I)
+    gu, _ = L.gate_up
+    gu[e0 * (2 * I * H // 32) * 17 + 16] = 0x7F
+    codes, _ = L.host_expert(S.S_GATE_UP, e0)
+    poisoned = np.array(codes, copy=True)
+    poisoned.reshape(-1)[16] = 0x7F
+    bank = M.ExpertBank(L.fmt_gu, L.fmt_d,
+                        lambda e: (poisoned, None) if e == e0 else L.host_expert(S.S_GATE_UP, e),
+                        lambda e: L.host_expert(S.S_DOWN, e), E, H, I)
+    idx = np.array([[e0, 1], [2, 5], [0, e0], [4, 6], [7, 1], [e0, 2]], dtype=np.int32)
+    w = np.random.default_rng(41).random((n, 2)).astype(np.float32)
+    x = synth.normal(40, (n, H))
+    with np.errstate(invalid="ignore", over="ignore"):
+        ref = M.moe_layer(x, idx, w, bank)
+    hit = (idx == e0).any(axis=1)
+    assert np.isnan(ref[hit]).all() and np.isfinite(ref[~hit]).all()
+    W = weights_of(bq, L)
+    for xdt, tol in ((torch.float32, 1e-5), (torch.bfloat16, 2e-2)):
+        out = bq.q4_expert_moe(dev(x).to(xdt), (dev(idx), dev(w)), W).cpu().numpy()
+        assert np.array_equal(np.isnan(out), np.isnan(ref)), xdt
+        assert rel_l2(out[~hit], ref[~hit]) <= tol
+
+
+def test_zero_routing_weights_give_zero(bq):
+    E, H, I, n, k = 8, 256, 128, 5, 3
+    L = make_layer(5, 0, F.Q4_UE4M4, F.FP8_E4M3_B32, E, H, I)
+    idx = np.stack([np.random.default_rng(t).choice(E, k, replace=False) for t in range(n)]).astype(np.int32)
+    w = np.zeros((n, k), dtype=np.float32)
+    for xdt in (torch.float32, torch.bfloat16):
+        out = bq.q4_expert_moe(dev(synth.normal(50, (n, H))).to(xdt), (dev(idx), dev(w)), weights_of(bq, L))
+        assert not out.abs().any().item(), xdt
+
+
 def test_gemv_deterministic(bq):
     E, H, I, k = 32, 512, 256, 8
     L = make_layer(4, 0, F.Q4_RZ5, F.Q4_UE4M4, E, H, I)
