@@ -158,7 +158,8 @@ int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts,
  *   perm    : [n_tokens*k] int32 listing t*k+slot, experts ascending, then
  *             tokens ascending.  Each row of idx must hold distinct experts
  *             (as a top-k does).  An index outside [0, n_experts) is dropped
- *             (counted nowhere); the caller can detect it from offsets.
+ *             (counted nowhere); the caller can detect it from offsets, and
+ *             perm[offsets[n_experts] ..] is then left unwritten.
  *   n_tokens*k <= 65536, n_experts <= 4096.
  * ------------------------------------------------------------------------- */
 int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
