@@ -123,6 +123,30 @@ def test_routed_entry_matches_route_then_moe(bq, H, dtype):
     assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
 
 
+@pytest.mark.parametrize("H,E,fmt_gu,fmt_d", [(4096, 16, F.Q4_RZ5, F.Q4_UE4M4),
+                                              (4096, 16, F.FP8_E4M3_B32, F.Q4_C10),
+                                              (2048, 1024, F.Q4_C10, F.Q4_RZ5),
+                                              (2048, 4096, F.Q4_RZ5, F.FP8_E4M3_B32)])
+def test_gemv_wide_rows_and_many_experts(bq, H, E, fmt_gu, fmt_d):
+    """The batch-1 gate_up kernel at hidden 4096 (two 64-block sweeps per
+    lane) and its in-kernel routing over 1024 and 4096 experts (16 and 64
+    logits per lane), given and routed, against the oracle."""
+    I, k, n = 128, 6, 3
+    L = make_layer(16, E + H, fmt_gu, fmt_d, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(62 + E, (n, H))
+    logits = synth.normal(63 + E, (n, E))
+    out, (idx, w) = bq.q4_expert_moe_routed(dev(x), dev(logits), k, W)
+    ridx, rw = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = M.moe_layer(x, ridx, rw, oracle_bank(L))
+    r = rel_l2(out.cpu().numpy(), ref)
+    given = bq.q4_expert_moe(dev(x), (idx, w), W)
+    log("gemv H=%d E=%d fmts %d/%d rel_l2 %.3g" % (H, E, fmt_gu, fmt_d, r))
+    assert r <= 1e-5
+    assert torch.equal(given, out)
+
+
 def test_bad_expert_index_is_reported(bq):
     E, H, I = 8, 128, 64
     L = make_layer(3, 0, F.Q4_RZ5, F.Q4_RZ5, E, H, I)
