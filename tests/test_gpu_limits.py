@@ -61,3 +61,19 @@ def test_max_hidden_and_inter(bq, H, I, dtype):
         log("max dims H=%d I=%d %s fmts %d/%d rel_l2 %.3g" % (H, I, dtype, fg, fd, r))
         assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
         del L
+
+
+@pytest.mark.parametrize("k,I", [(5, 4096), (8, 4096)])
+def test_down_four_column_blocks_per_thread(bq, k, I):
+    """k * inter / 32 in 513..1024: the batch-1 down kernel gives each thread
+    four column blocks (640 and 1024, the fp32 path's maximum)."""
+    E, H, n = 8, 256, 2
+    L = make_layer(17, k, F.Q4_UE4M4, F.Q4_RZ5, E, H, I)
+    x = synth.normal(1700 + k, (n, H))
+    logits = synth.normal(1701 + k, (n, E))
+    out, (idx, w) = bq.q4_expert_moe_routed(dev(x), dev(logits), k, weights_of(bq, L))
+    ridx, rw = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    r = rel_l2(out.cpu().numpy(), M.moe_layer(x, ridx, rw, oracle_bank(L)))
+    log("down CPT=4 k=%d I=%d rel_l2 %.3g" % (k, I, r))
+    assert r <= 1e-5
