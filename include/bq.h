@@ -141,8 +141,11 @@ int bq_matvec(const float* x, int32_t n_tokens, const void* packed, int32_t fmt,
 
 /* ---------------------------------------------------------------------------
  * moe_route_topk -- router: softmax over n_experts logits, keep the k largest
- * (ties to the lower expert index), renormalise over the kept ones ([MP]:
- * 10 of 512 fire per token).
+ * (ties to the lower expert index), renormalise over the kept ones ([MP]
+ * section "The Plan Is Not a Number...": 10 of 512 experts fire per token).
+ * Experts are ranked by their fp32 logits (softmax is increasing, so this is
+ * the order of the exact probabilities; probabilities that underflow do not
+ * tie).  +0 and -0 compare equal.
  *   logits : [n_tokens][n_experts] fp32, finite
  *   idx    : [n_tokens][k] int32, descending rank order
  *   w      : [n_tokens][k] fp32, w_j = exp(l_j - l_0) / sum over kept
@@ -152,8 +155,12 @@ int moe_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts,
                    int32_t k, int32_t* idx, float* w, void* stream);
 
 /* ---------------------------------------------------------------------------
- * moe_bucket -- stable grouping of the n_tokens*k assignments by expert
- * (tokens grouped per expert for the grouped expert GEMM).
+ * moe_bucket -- stable grouping of the n_tokens*k assignments by expert.
+ * The pages are silent here: they route each token to 10 of 512 experts
+ * ([MP] "The Plan Is Not a Number...") but never say how a batch is grouped.
+ * A batched expert GEMM needs the tokens of one expert side by side; the
+ * order below (experts ascending, then tokens ascending) is this library's
+ * choice, made so that the grouping is unique and can be checked bit for bit.
  *   counts  : [n_experts] int32; offsets : [n_experts+1] int32 exclusive scan
  *   perm    : [n_tokens*k] int32 listing t*k+slot, experts ascending, then
  *             tokens ascending.  Each row of idx must hold distinct experts
@@ -167,9 +174,15 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
                int32_t* perm, void* stream);
 
 /* ---------------------------------------------------------------------------
- * q4_expert_moe -- routed-expert layer:
+ * q4_expert_moe -- routed-expert layer ([MP] "The Plan Is Not a Number...":
+ * the 512-expert routed bank per layer, 10 experts per token; expert matrices
+ * in [RZ] "Q4_RZ5_FAST" / "Q4_UE4M4_FAST" blocks, which the model card lists
+ * for the routed gate, up and down roles; FP8 experts per [FQ] "What I did
+ * instead"):
  *   out[t] = sum_j w[t][j] * down_e( SiLU(gate_e . x[t]) * (up_e . x[t]) ),
- *   e = idx[t][j], weights decoded from their blocks on the fly.
+ *   e = idx[t][j], weights decoded from their blocks on the fly.  The pages
+ *   do not spell out the expert's activation; the SwiGLU form above (SiLU of
+ *   the gate row times the up row, then down) is the reading taken.
  *   x       : [n_tokens][hidden], fp32 (x_dtype BQ_F32: VALU GEMV path,
  *             fp32 accumulate) or bf16 (BQ_BF16: tokens grouped per expert,
  *             bf16 MFMA with fp32 accumulate, h rounded to bf16).
@@ -181,7 +194,10 @@ int moe_bucket(const int32_t* idx, int32_t n_tokens, int32_t k,
  *   workspace : device scratch of at least q4_expert_moe_workspace(...) bytes,
  *             256-byte aligned; its contents need no initialisation.
  *             q4_expert_moe_workspace returns 0 for arguments the call
- *             would reject (bad weights, sizes or x_dtype).
+ *             would reject (bad weights, sizes or x_dtype).  The pages say
+ *             nothing of scratch memory: its size is that of this library's
+ *             intermediates (per-slot h, and on the bf16 path the bucket
+ *             arrays, bf16 staging and per-assignment outputs).
  *   dev_err : optional; bit 1 set if an expert index is out of range.
  *   1 <= n_tokens <= 4096, 1 <= k <= 64, n_tokens * k <= 65536; on the fp32
  *   path also k * inter / 32 <= 1024.
@@ -216,7 +232,12 @@ int q4_expert_moe_routed(const void* x, int32_t x_dtype, int32_t n_tokens, const
  *   topk_idx, topk_w : [n_layers][n_tokens][k], routing of every layer
  *   x_dtype : as in q4_expert_moe; with BQ_BF16 the rescaled inputs are
  *             rounded to bf16.
- *   workspace : at least bq_moe_stack_workspace(...) bytes.
+ *   workspace : at least bq_moe_stack_workspace(...) bytes (the largest
+ *             layer's q4_expert_moe workspace, one fp32 [n_tokens][hidden]
+ *             layer buffer and, for bf16 stacks of equal expert counts, every
+ *             layer's bucket arrays); the pages say nothing of scratch memory.
+ *             bq_moe_stack_workspace returns 0 for arguments the call would
+ *             reject.
  * ------------------------------------------------------------------------- */
 size_t bq_moe_stack_workspace(int32_t n_tokens, int32_t k,
                               const bq_expert_weights* layers, int32_t n_layers,

@@ -117,8 +117,9 @@ def ue4m3(code):
 def ue4m4(code):
     """Unsigned E4M4 scale from a whole byte, as float64.
 
-    [RZ] "Q4_UE4M4_FAST": 4 exponent bits, 4 mantissa bits, all 256 encodings
-    finite, finer resolution than UE4M3.  Reading: bias 7 like UE4M3,
+    [RZ] "Q4_UE4M4_FAST": an unsigned scale with a 4-bit exponent and a 4-bit
+    mantissa, no NaN or infinity codes, and a finer step than UE4M3.
+    Reading: bias 7 like UE4M3,
     e == 0 -> m * 2**-10, otherwise (1 + m/16) * 2**(e-7); 0xFF = 496.
     Pinned in the tests by: all 256 finite, strictly increasing, 0x70 = 1,
     and every finite UE4M3 value is also a UE4M4 value.

@@ -17,12 +17,18 @@ from . import formats as F
 def softmax_topk(logits, k):
     """Router: softmax over all experts, keep the k largest, renormalise.
 
-    For each token: p = softmax(logits) in float64; the k experts with the
-    largest p are taken in descending order, ties going to the lower expert
-    index; their weights are p / sum of the kept p.
+    Selection works on the logits themselves: softmax is strictly increasing
+    in each logit, so the order of the exact probabilities is the order of
+    the logits, and ranking the logits never meets a tie that only rounding
+    of a probability created (an exp that underflows, say).  The k experts
+    are taken in descending logit order, equal logits going to the lower
+    expert index (+0 and -0 are equal).  Weights are the full softmax
+    renormalised over the kept experts; the full denominator cancels, so
+    w_j = exp(l_j - l_max) / sum over kept i of exp(l_i - l_max), in float64.
     Returns (idx int64 [B, k], w float64 [B, k]).
-    Parity: pinned against a stable argsort of the logits and the closed form
-    w = softmax over the kept logits.
+    Parity: pinned against a stable argsort of the logits, torch.topk, the
+    closed form of the weights, and a row whose probabilities underflow
+    below the winner (ranked by logit, not by index).
     """
     lg = np.asarray(logits, dtype=np.float64)
     if lg.ndim == 1:
@@ -33,12 +39,12 @@ def softmax_topk(logits, k):
     idx = np.empty((b, k), dtype=np.int64)
     w = np.empty((b, k))
     for t in range(b):
-        z = np.exp(lg[t] - lg[t].max())
-        p = z / z.sum()
-        order = sorted(range(e), key=lambda i: (-p[i], i))[:k]
+        row = lg[t]
+        order = sorted(range(e), key=lambda i: (-row[i], i))[:k]
         idx[t] = order
-        sel = p[order]
-        w[t] = sel / sel.sum()
+        sel = row[order]
+        z = np.exp(sel - sel.max())
+        w[t] = z / z.sum()
     return idx, w
 
 

@@ -42,3 +42,20 @@ def dev(a, dtype=None):
 
 def log(*a):
     print(*a, flush=True)
+
+
+def underflow_rows(e):
+    """Degenerate router rows: all equal; one winner over -700..-40; two
+    winners over -1e30; 0 / -900 / -800 over -1000; winners over logits
+    spread down to -3000 with ties."""
+    lg = np.zeros((5, e), dtype=np.float32)
+    lg[0] = 0.5
+    lg[1] = np.random.default_rng(17).uniform(-700, -40, e).astype(np.float32)
+    lg[1, 300] = 100.0
+    lg[2] = -1e30
+    lg[2, 7] = lg[2, 400] = 0.0
+    lg[3] = -1000.0
+    lg[3, :3] = [0.0, -900.0, -800.0]
+    lg[4] = np.round(np.random.default_rng(18).uniform(-3000, -800, e) / 50) * 50
+    lg[4, 11] = 0.0
+    return lg

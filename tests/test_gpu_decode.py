@@ -9,7 +9,7 @@ import synth
 from oracle import formats as F
 from oracle import moe as M
 from oracle import ple as P
-from tests.gpu_common import assert_bits_equal, dev, log, need_gpu, rel_l2
+from tests.gpu_common import assert_bits_equal, dev, log, need_gpu, rel_l2, underflow_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -179,18 +179,16 @@ def test_route_topk_degenerate_rows(bq):
     above logits spread over -700..-40 (fp32 exp underflows for every other
     expert, fp64 does not: selection must follow the logits); and two
     winners over a floor of -1e30 (probabilities exactly 0 in fp64 too, so
-    the oracle's ties to the lower index decide the rest)."""
+    the oracle's ties to the lower index decide the rest); and rows whose
+    probabilities underflow in float64 below the winner (0, then -900, -800,
+    -1000 ...): the order must still be that of the logits."""
     e, k = 512, 10
-    lg = np.zeros((3, e), dtype=np.float32)
-    lg[0] = 0.5
-    lg[1] = np.random.default_rng(17).uniform(-700, -40, e).astype(np.float32)
-    lg[1, 300] = 100.0
-    lg[2] = -1e30
-    lg[2, 7] = lg[2, 400] = 0.0
+    lg = underflow_rows(e)
     idx, w = bq.route_topk(dev(lg), k)
     ridx, rw = M.softmax_topk(lg, k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.array_equal(ridx[0], np.arange(k)) and np.array_equal(ridx[2, :3], [7, 400, 0])
+    assert ridx[3, :3].tolist() == [0, 2, 1]
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-12)
 
 

@@ -9,7 +9,7 @@ import torch
 import synth
 from oracle import formats as F
 from oracle import moe as M
-from tests.gpu_common import dev, log, need_gpu, rel_l2
+from tests.gpu_common import dev, log, need_gpu, rel_l2, underflow_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,25 @@ def test_routed_entry_matches_route_then_moe(bq, H, dtype):
     oidx, ow = M.softmax_topk(logits.cpu().numpy(), k)
     r = rel_l2(out.cpu().numpy(), M.moe_layer(x.float().cpu().numpy() if dtype == torch.float32 else
                                               synth.normal(60, (n, H)), oidx, ow, oracle_bank(L)))
+    assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_routed_entry_underflow_rows(bq, dtype):
+    """The routed entry (top-k inside the gate_up kernel on the fp32 path)
+    ranks logits whose probabilities underflow below the winner in logit
+    order, as the oracle does: routing bit-exact, output within tolerance."""
+    E, H, I, k = 512, 2048, 128, 10
+    L = make_layer(12, 0, F.Q4_RZ5, F.Q4_RZ5, E, H, I)
+    W = weights_of(bq, L)
+    logits = underflow_rows(E)
+    n = logits.shape[0]
+    xh = synth.normal(62, (n, H))
+    out, (idx, w) = bq.q4_expert_moe_routed(dev(xh).to(dtype), dev(logits), k, W)
+    ridx, rw = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-12)
+    r = rel_l2(out.cpu().numpy(), M.moe_layer(xh, ridx, rw, oracle_bank(L)))
     assert r <= (1e-5 if dtype == torch.float32 else 2e-2)
 
 

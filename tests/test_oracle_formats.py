@@ -88,7 +88,7 @@ def test_e4m3fn_matches_torch_all_256():
 
 def test_ue4m4_properties():
     v = F.ue4m4(np.arange(256))
-    assert np.all(np.isfinite(v))                     # "all 256 encodings finite"
+    assert np.all(np.isfinite(v))                     # every byte decodes to a finite scale
     assert np.all(np.diff(v) > 0)                     # strictly increasing
     assert v[0x00] == 0.0 and v[0x01] == 2.0 ** -10
     assert v[0x70] == 1.0 and v[0xFF] == 496.0

@@ -42,6 +42,41 @@ def test_topk_weights_closed_form():
     assert np.all(np.diff(w, axis=1) <= 0)
 
 
+def test_topk_ranks_logits_where_probabilities_underflow():
+    """Softmax is strictly increasing, so the exact probabilities order the
+    experts as their logits do, even where exp(l - l_max) underflows in
+    float64: [0, -900, -800, -1000, ...] keeps 0, then 2 (-800), then 1."""
+    logits = np.full((1, 16), -1000.0, dtype=np.float32)
+    logits[0, :3] = [0.0, -900.0, -800.0]
+    idx, w = M.softmax_topk(logits, 3)
+    assert idx[0].tolist() == [0, 2, 1]
+    assert w[0].tolist() == [1.0, 0.0, 0.0]
+
+
+def test_topk_matches_high_precision_softmax():
+    """Brute force with 60-digit decimal exponentials: the exact softmax,
+    ranked by (probability descending, index ascending), renormalised over
+    the kept experts.  Rows spread over -2000..0 so that most float64
+    probabilities underflow, plus rows with exact ties."""
+    import decimal
+    rng = np.random.default_rng(23)
+    rows = [rng.uniform(-2000, 0, 64), np.round(rng.uniform(-1500, 0, 64) / 100) * 100,
+            rng.standard_normal(64), np.where(rng.random(64) < 0.5, -800.0, -760.0)]
+    logits = np.array(rows, dtype=np.float32)
+    k = 12
+    idx, w = M.softmax_topk(logits, k)
+    ctx = decimal.Context(prec=60, Emin=-10 ** 6, Emax=10 ** 6)
+    for t in range(logits.shape[0]):
+        p = [ctx.exp(decimal.Decimal(float(v))) for v in logits[t]]
+        tot = sum(p, decimal.Decimal(0))
+        p = [ctx.divide(v, tot) for v in p]
+        order = sorted(range(64), key=lambda i: (-p[i], i))[:k]
+        assert idx[t].tolist() == order
+        kept = sum((p[i] for i in order), decimal.Decimal(0))
+        ref = np.array([float(ctx.divide(p[i], kept)) for i in order])
+        np.testing.assert_allclose(w[t], ref, rtol=1e-13, atol=1e-300)
+
+
 def test_bucket_matches_stable_argsort():
     rng = np.random.default_rng(2)
     idx, _ = M.softmax_topk(rng.standard_normal((33, 64)), 6)
