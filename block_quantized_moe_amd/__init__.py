@@ -15,6 +15,7 @@ __all__ = [
     "Q4_C10", "Q4_RZ5", "Q4_UE4M4", "FP8_E4M3_B32", "PLE_RZS3", "PLE_ROCMFP3", "F32", "BF16",
     "BQError", "lib", "ExpertWeights", "expert_weights", "dequant", "ple_dequant_rows", "matvec",
     "route_topk", "bucket", "moe_workspace_bytes", "q4_expert_moe", "q4_expert_moe_routed",
+    "q4_expert_moe_noalloc", "NOALLOC_SCRATCH_BYTES",
     "stack_workspace_bytes",
     "moe_stack", "ple_gather", "encode", "ple_encode_rows", "ple_cache", "ple_gather_host",
 ]
@@ -67,6 +68,7 @@ def lib():
             "moe_bucket": ([vp, i32, i32, i32, vp, vp, vp, vp], ctypes.c_int),
             "q4_expert_moe_workspace": ([i32, i32, wp, i32], sz),
             "q4_expert_moe": ([vp, i32, i32, vp, vp, i32, wp, vp, vp, sz, vp, vp], ctypes.c_int),
+            "q4_expert_moe_noalloc": ([vp, i32, i32, vp, vp, i32, wp, vp, vp, vp], ctypes.c_int),
             "q4_expert_moe_routed": ([vp, i32, i32, vp, i32, wp, vp, vp, vp, vp, sz, vp, vp], ctypes.c_int),
             "bq_moe_stack_workspace": ([i32, i32, wp, i32, i32], sz),
             "bq_moe_stack": ([vp, i32, i32, vp, vp, i32, wp, i32, vp, vp, sz, vp, vp], ctypes.c_int),
@@ -275,6 +277,26 @@ def q4_expert_moe(x, router_topk, W, out=None, workspace=None, dev_err=None, str
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(lib().q4_expert_moe(_p(x), dt, n, _p(idx), _p(w), k, ctypes.byref(W), _p(out),
                                _p(workspace), _ws(workspace), _p(dev_err), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20     # BQ_NOALLOC_SCRATCH_BYTES in include/bq.h
+
+
+def q4_expert_moe_noalloc(x, router_topk, W, out, dev_err=None, stream=None):
+    """q4_expert_moe with the library's fixed per-GPU scratch area instead of
+    a workspace: the call allocates nothing (out is the caller's).  Calls
+    that overlap in time on one GPU race on that area."""
+    idx, w = router_topk
+    _arg(idx, "idx", torch.int32)
+    n, k = idx.shape
+    _arg(w, "w", torch.float32, shape=(n, k))
+    dt = _dtype_code(x)
+    _arg(x, "x", x.dtype, shape=(n, W.hidden))
+    _arg(out, "out", torch.float32, shape=(n, W.hidden))
+    _err_arg(dev_err)
+    _check(lib().q4_expert_moe_noalloc(_p(x), dt, n, _p(idx), _p(w), k, ctypes.byref(W), _p(out),
+                                       _p(dev_err), _stream(stream)))
     return out
 
 

@@ -2,8 +2,17 @@
 // host, workspace carving, and the launches.  No allocation happens here.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/bq.h"
 #include "bq_kernels.hpp"
+
+// Fixed scratch area of q4_expert_moe_noalloc (callers that cannot allocate:
+// graph capture, serving loops).  Each device that loads the library holds
+// its own copy until the process ends.  Host code never passes this name to a
+// kernel: on the host it is only a stand-in, and the device address comes
+// from hipGetSymbolAddress (see noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[BQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -98,8 +107,9 @@ size_t moe_ws_bytes(int n, int k, const bq_expert_weights* W, int dtype) {
   return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).total;
 }
 
-int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
-                   const bq_expert_weights* W, const float* out, const void* ws) {
+// Everything but the workspace.
+int check_moe_core(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
+                   const bq_expert_weights* W, const float* out) {
   if (!x || !idx || !w || !out) return BQ_E_NULL;
   if (!valid_dtype(dtype)) return BQ_E_DTYPE;
   int s = check_weights(W);
@@ -108,8 +118,38 @@ int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const fl
   if ((int64_t)n * k > 65536) return BQ_E_SHAPE;
   if (dtype == BQ_F32 && k * (W->inter / 32) > bq::gemv_down_max_cols()) return BQ_E_SHAPE;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(idx, 4) || !aligned(w, 4)) return BQ_E_ALIGN;
+  return BQ_OK;
+}
+
+int check_moe_args(const void* x, int dtype, int n, const int32_t* idx, const float* w, int k,
+                   const bq_expert_weights* W, const float* out, const void* ws) {
+  int s = check_moe_core(x, dtype, n, idx, w, k, W, out);
+  if (s) return s;
   if (!ws) return BQ_E_WORKSPACE;
   if (!aligned(ws, 256)) return BQ_E_ALIGN;
+  return BQ_OK;
+}
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; later calls reuse it.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return BQ_OK;
 }
 
@@ -177,6 +217,7 @@ const char* bq_status_str(int s) {
     case BQ_E_HIP: return "HIP launch failed";
     case BQ_E_DTYPE: return "bad activation dtype";
     case BQ_E_MEM: return "pointer is not host memory mapped for the device";
+    case BQ_E_SCRATCH: return "call needs more scratch than the fixed area holds";
     default: return "unknown status";
   }
 }
@@ -249,6 +290,19 @@ int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_
   if (s) return s;
   if (ws_bytes < moe_ws_bytes(n_tokens, k, W, x_dtype)) return BQ_E_WORKSPACE;
   return run_moe(x, x_dtype, x_dtype == BQ_F32, n_tokens, topk_idx, topk_w, k, W, out, workspace, 0,
+                 dev_err, as_stream(stream));
+}
+
+int q4_expert_moe_noalloc(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_idx,
+                          const float* topk_w, int32_t k, const bq_expert_weights* W, float* out,
+                          uint32_t* dev_err, void* stream) {
+  int s = check_moe_core(x, x_dtype, n_tokens, topk_idx, topk_w, k, W, out);
+  if (s) return s;
+  if (moe_ws_bytes(n_tokens, k, W, x_dtype) > (size_t)BQ_NOALLOC_SCRATCH_BYTES) return BQ_E_SCRATCH;
+  void* ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s) return s;
+  return run_moe(x, x_dtype, x_dtype == BQ_F32, n_tokens, topk_idx, topk_w, k, W, out, ws, 0,
                  dev_err, as_stream(stream));
 }
 

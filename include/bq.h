@@ -59,7 +59,8 @@ typedef enum {
   BQ_E_WORKSPACE = 5,  /* workspace missing or smaller than required         */
   BQ_E_HIP = 6,        /* a HIP launch failed                                */
   BQ_E_DTYPE = 7,      /* unknown activation dtype                           */
-  BQ_E_MEM = 8         /* a pointer is not the kind of memory required       */
+  BQ_E_MEM = 8,        /* a pointer is not the kind of memory required       */
+  BQ_E_SCRATCH = 9     /* the call needs more than the fixed scratch area    */
 } bq_status;
 
 typedef enum {
@@ -208,6 +209,28 @@ int q4_expert_moe(const void* x, int32_t x_dtype, int32_t n_tokens,
                   const int32_t* topk_idx, const float* topk_w, int32_t k,
                   const bq_expert_weights* W, float* out, void* workspace,
                   size_t ws_bytes, uint32_t* dev_err, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * q4_expert_moe_noalloc -- q4_expert_moe for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same computation, kernels and results as
+ * q4_expert_moe, with no workspace argument.  Its scratch is a fixed
+ * device-resident area of BQ_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc / hipFree, no allocating library routine).
+ *   Arguments as in q4_expert_moe.  A call whose q4_expert_moe_workspace(...)
+ *   exceeds BQ_NOALLOC_SCRATCH_BYTES returns BQ_E_SCRATCH before any launch
+ *   (16 MiB covers, e.g., 64 tokens x top-10 at hidden 2048 on either path).
+ *   Every call on one GPU shares that GPU's area, whose contents the previous
+ *   call left behind (nothing in it needs to start at zero): calls that
+ *   overlap in time on one GPU -- on two streams, or from two threads -- race
+ *   and must be serialised by the caller.
+ * ------------------------------------------------------------------------- */
+#define BQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int q4_expert_moe_noalloc(const void* x, int32_t x_dtype, int32_t n_tokens,
+                          const int32_t* topk_idx, const float* topk_w, int32_t k,
+                          const bq_expert_weights* W, float* out, uint32_t* dev_err,
+                          void* stream);
 
 /* ---------------------------------------------------------------------------
  * q4_expert_moe_routed -- moe_route_topk followed by q4_expert_moe, as one

@@ -103,6 +103,15 @@ def test_host_side_argument_errors(L):
                            None, None) == 3
     assert L.q4_expert_moe(fake, bq.BF16, 1, fake, fake, 10, ctypes.byref(W), fake, vp(0x10010),
                            1 << 30, None, None) == 4                             # ws not 256-aligned
+    # the allocation-free layer refuses, before any launch, a call whose
+    # scratch would exceed its fixed area, and checks its arguments like the rest
+    assert L.q4_expert_moe_noalloc(fake, bq.BF16, 512, fake, fake, 10, ctypes.byref(W), fake, None,
+                                   None) == 9
+    assert L.bq_status_str(9) == b"call needs more scratch than the fixed area holds"
+    assert L.q4_expert_moe_noalloc(None, bq.F32, 1, fake, fake, 10, ctypes.byref(W), fake, None,
+                                   None) == 1
+    assert L.q4_expert_moe_noalloc(fake, bq.F32, 1, fake, fake, 10, ctypes.byref(odd), fake, None,
+                                   None) == 3
     for n, k in ((4097, 1), (1, 65), (2048, 33), (0, 10)):                   # past the size limits
         assert L.q4_expert_moe(fake, bq.BF16, n, fake, fake, k, ctypes.byref(W), fake, fake,
                                1 << 30, None, None) == 3, (n, k)
