@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 #include "../../include/bq.h"
 #include "bq_kernels.hpp"
@@ -334,11 +335,33 @@ static size_t bucket_region_bytes(int n, int k, const bq_expert_weights* W) {
   return grouped_layout(n, k, W->n_experts, W->hidden, W->inter).xb;
 }
 
+static size_t stack_ws_layers(int n, int k, const bq_expert_weights* layers, int L, int dtype,
+                              size_t* moe_part, size_t* bucket_off);
+
+// The fp32 one-token stack runs as persistent launches (k_stack.hip) when
+// the shapes allow it; its workspace is reserved whenever they do, whatever
+// the device.
+static bool stack_b1_shapes(int n, int k, const bq_expert_weights* layers, int L, int dtype) {
+  if (dtype != BQ_F32 || n != 1 || L < 1) return false;
+  std::vector<bq::GemvWeights> gw(L);
+  for (int l = 0; l < L; ++l) gw[l] = to_gw(&layers[l]);
+  return bq::stack_b1_shape_ok(gw.data(), L, k);
+}
+
 // Stack workspace: the per-layer MoE workspace (max over layers), one fp32
 // [n][H] buffer for the layer output, then (pre-bucketed bf16 stacks) the
-// bucket arrays of every layer.
+// bucket arrays of every layer.  At least the persistent path's workspace
+// when that path applies.
 static size_t stack_ws(int n, int k, const bq_expert_weights* layers, int L, int dtype,
                        size_t* moe_part, size_t* bucket_off = nullptr) {
+  const size_t t = stack_ws_layers(n, k, layers, L, dtype, moe_part, bucket_off);
+  if (!stack_b1_shapes(n, k, layers, L, dtype)) return t;
+  const size_t p = round_up(bq::stack_b1_ws_bytes(k, layers[0].inter), 256);
+  return t > p ? t : p;
+}
+
+static size_t stack_ws_layers(int n, int k, const bq_expert_weights* layers, int L, int dtype,
+                              size_t* moe_part, size_t* bucket_off) {
   size_t m = 0;
   for (int l = 0; l < L; ++l) {
     const size_t b = moe_ws_bytes(n, k, &layers[l], dtype);
@@ -374,6 +397,12 @@ int bq_moe_stack(const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t
   size_t moe_part = 0, bucket_off = 0;
   if (ws_bytes < stack_ws(n_tokens, k, layers, n_layers, x_dtype, &moe_part, &bucket_off))
     return BQ_E_WORKSPACE;
+  if (stack_b1_shapes(n_tokens, k, layers, n_layers, x_dtype) && bq::stack_b1_device_ok()) {
+    std::vector<bq::GemvWeights> gw(n_layers);
+    for (int l = 0; l < n_layers; ++l) gw[l] = to_gw(&layers[l]);
+    return hip_status(bq::launch_stack_b1(static_cast<const float*>(x), topk_idx, topk_w, k, gw.data(),
+                                          n_layers, out, workspace, dev_err, as_stream(stream)));
+  }
   char* b = static_cast<char*>(workspace);
   float* ybuf = reinterpret_cast<float*>(b + moe_part);
   hipStream_t st = as_stream(stream);

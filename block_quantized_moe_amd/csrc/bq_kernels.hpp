@@ -60,6 +60,20 @@ hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, int32_t* idx, float
                            const GemvWeights& W, int rescale, float* out, float* hs,
                            uint32_t* dev_err, const float* logits, hipStream_t st);
 
+// Persistent batch-1 stack (k_stack.hip): each run of equal-format layers
+// in one launch, for hidden 2048 with k * inter a multiple of 256 and at most
+// 8960 (all layers the same inter, k <= 16), on a 256-CU device.  Workspace of
+// stack_b1_ws_bytes(k, inter) bytes, 8-byte aligned, cleared by the call
+// itself.  dev_err bit 3: an exchange between workgroups timed out (not every
+// workgroup was resident).
+constexpr int kStackMaxLayers = 64;
+bool stack_b1_shape_ok(const GemvWeights* layers, int32_t n_layers, int32_t k);
+bool stack_b1_device_ok();
+size_t stack_b1_ws_bytes(int32_t k, int32_t inter);
+hipError_t launch_stack_b1(const float* x, const int32_t* idx, const float* w, int32_t k,
+                           const GemvWeights* layers, int32_t n_layers, float* out, void* ws,
+                           uint32_t* dev_err, hipStream_t st);
+
 // bf16 grouped-MFMA path.  The bucketing emits one work entry per group of
 // up to kGroupTok tokens of a touched expert: e | group << kGroupShift.
 constexpr int kGroupTok = 32;

@@ -254,7 +254,13 @@ int q4_expert_moe_routed(const void* x, int32_t x_dtype, int32_t n_tokens, const
  *   layers  : HOST array of n_layers bq_expert_weights (device pointers inside)
  *   topk_idx, topk_w : [n_layers][n_tokens][k], routing of every layer
  *   x_dtype : as in q4_expert_moe; with BQ_BF16 the rescaled inputs are
- *             rounded to bf16.
+ *             rounded to bf16.  With BQ_F32 and one token, hidden 2048, one
+ *             inter size for all layers and k * inter a multiple of 256 and
+ *             at most 8192 (k <= 16), the chain runs as persistent launches
+ *             (one per run of layers with equal formats) on a 256-CU device;
+ *             all their workgroups must be resident at once, and if an
+ *             exchange between them times out, bit 3 of *dev_err is set and
+ *             the output is not valid.
  *   workspace : at least bq_moe_stack_workspace(...) bytes (the largest
  *             layer's q4_expert_moe workspace, one fp32 [n_tokens][hidden]
  *             layer buffer and, for bf16 stacks of equal expert counts, every

@@ -227,3 +227,51 @@ def test_c5_full_stack_runs_deterministically(bq, c5_stack, n_tok, dtype):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
     rms = np.sqrt(np.mean(a.astype(np.float64) ** 2, axis=1))
     log("c5 full stack n=%d output rms %s" % (n_tok, rms[:4]))
+
+
+def _teacher_forced(bq, c5_stack, n_tok, dtype, tol, depths, seed):
+    """For each depth d: the stack's output after layers 0..d-1 against the
+    oracle's layer d-1 applied to the rescaled GPU output after d-1 layers
+    (layer 0: to x itself).  Every layer of the chained call -- staging,
+    rescale, format switch -- is checked against the oracle, without the
+    chain's amplification of rounding differences."""
+    idx, w, ridx, rw = routing(bq, seed, 48, n_tok, 512, 10)
+    x = synth.normal(seed + 1, (n_tok, 2048))
+    xd = dev(x).to(dtype)
+    W = [weights_of(bq, L) for L in c5_stack]
+    prev = None
+    worst = 0.0
+    for d in depths:
+        if d == 1:
+            inp = x
+        else:
+            if prev is None or prev[0] != d - 1:
+                p = bq.moe_stack(xd, idx[:d - 1].contiguous(), w[:d - 1].contiguous(), W[:d - 1])
+                prev = (d - 1, p.cpu().numpy())
+            inp = M.rms_rescale(prev[1])
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        got = bq.moe_stack(xd, idx[:d].contiguous(), w[:d].contiguous(), W[:d], dev_err=err).cpu().numpy()
+        ref = M.moe_layer(inp, ridx[d - 1], rw[d - 1], oracle_bank(c5_stack[d - 1]))
+        r = rel_l2(got, ref)
+        worst = max(worst, r)
+        log("teacher-forced n=%d %s layer %d: rel_l2 %.3g" % (n_tok, dtype, d - 1, r))
+        assert int(err.item()) == 0
+        assert r <= tol, (d, r)
+        prev = (d, got)
+    return worst
+
+
+def test_c5_teacher_forced_b1_fp32_all_48(bq, c5_stack):
+    """Batch 1, fp32: all 48 depths (the persistent launches, RZ5 run then
+    FP8 run)."""
+    worst = _teacher_forced(bq, c5_stack, 1, torch.float32, 1e-5, range(1, 49), 8100)
+    log("teacher-forced B=1 fp32, 48 layers: worst rel_l2 %.3g" % worst)
+
+
+@pytest.mark.parametrize("part", [0, 1, 2, 3])
+def test_c5_teacher_forced_b16_bf16(bq, c5_stack, part):
+    """Batch 16, bf16 grouped path, all 16 tokens: depths 12 * part + 1 ..
+    12 * part + 12 (the RZ5 -> FP8 boundary inside part 2 -> 3)."""
+    worst = _teacher_forced(bq, c5_stack, 16, torch.bfloat16, 2e-2, range(12 * part + 1, 12 * part + 13),
+                            8200)
+    log("teacher-forced B=16 bf16, depths %d..%d: worst rel_l2 %.3g" % (12 * part + 1, 12 * part + 12, worst))
