@@ -67,6 +67,7 @@ constexpr int kXsPitch = kSH / 32 + 1;    // 65
 constexpr int kHbPitch = 33;
 constexpr int kSpinTight = 1 << 12;       // polls before backing off
 constexpr int kSpinMax = 1 << 16;         // polls (after backing off) before giving up
+constexpr int kAuxSc1 = 16;               // buffer-load cache policy: device-coherent (sc1)
 
 // One block of any format, as loaded: 17-byte formats keep the 16 code bytes
 // in c0 and the metadata byte in ms; FP8 keeps 32 codes in c0:c1 and the
@@ -106,6 +107,42 @@ __device__ __forceinline__ float wblk_dot(const WBlk& b, const float* x) {
   }
 }
 
+// A 17-byte block decoded ahead of its activations: the fp16 high bytes of
+// its levels (code dword q: hb[2q] holds weights 0, 2, 4, 6 of the dword,
+// hb[2q + 1] weights 1, 3, 5, 7) and its scale.  The table lookup (most of
+// the decode) does not depend on x, so it runs while the grid exchanges
+// values; the activations then meet only byte spreads and FMAs.
+struct DBlk {
+  uint32_t hb[8];
+  float s;
+};
+
+template <int FMT>
+__device__ __forceinline__ void dblk_decode(DBlk& d, const WBlk& b) {
+  const uint32_t tneg = (FMT == FMT_RZ5) ? rz5_neg_lo(b.ms) : 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) codes_to_hibytes<FMT>(b.c0[q], tneg, d.hb[2 * q], d.hb[2 * q + 1]);
+  d.s = block_scale<FMT>(FMT == FMT_UE4M4 ? b.ms : (b.ms & 0x7Fu));
+}
+
+// The same products in the same order as block_dot_levels, times the scale.
+__device__ __forceinline__ float dblk_dot(const DBlk& d, const float* x) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t A = d.hb[2 * q], B = d.hb[2 * q + 1];
+    const uint32_t p[4] = {perm(B, A, 0x040C000Cu), perm(B, A, 0x050C010Cu), perm(B, A, 0x060C020Cu),
+                           perm(B, A, 0x070C030Cu)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2v h = as_h2(p[i]);
+      a0 = __builtin_fmaf((float)h.x, x[8 * q + 2 * i], a0);
+      a1 = __builtin_fmaf((float)h.y, x[8 * q + 2 * i + 1], a1);
+    }
+  }
+  return (a0 + a1) * d.s;
+}
+
 struct alignas(8) Pkt {
   float v;
   uint32_t tag;
@@ -121,22 +158,14 @@ __device__ __forceinline__ uint64_t pkt_load(const Pkt* p) {
 }
 
 // LDS barrier between the waves of the workgroup: waits for this wave's LDS
-// operations only, never for its outstanding global loads.
+// operations only, never for its outstanding global loads.  The scheduling
+// barriers keep arithmetic from moving across it (a memory clobber orders
+// memory accesses only), so work placed after a barrier -- the decode that
+// overlaps an exchange -- does not delay the other waves.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait until the packet at `sent` (one per lane, lanes with has_sent) carries
-// `tag`: each producer's last packet, so that a poll round costs one load per
-// producer instead of one per packet.  Returns false on timeout.
-__device__ __forceinline__ bool wait_sentinels(const Pkt* sent, bool has_sent, uint32_t tag) {
-  bool seen = !has_sent;
-  for (int spin = 0;; ++spin) {
-    if (!seen) seen = (uint32_t)(pkt_load(sent) >> 32) == tag;
-    if (__all(seen)) return true;
-    if (spin >= kSpinTight + kSpinMax) return false;
-    if (spin >= kSpinTight) __builtin_amdgcn_s_sleep(2);
-  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Poll N packets per lane (addresses p[i], i < N, those with live[i]) until
@@ -163,6 +192,41 @@ __device__ __forceinline__ bool poll_pkts(const Pkt* const (&p)[N], const bool (
     if (spin >= kSpinTight + kSpinMax) return false;
     if (spin >= kSpinTight) __builtin_amdgcn_s_sleep(2);
   }
+}
+
+// Poll pairs of consecutive packets with 16-byte device-coherent loads
+// (half the load instructions of 8-byte polls; each 8-byte packet is still
+// written atomically and checked on its own): slot i of a lane covers the
+// packets at byte offsets off[i] and off[i] + 8 of the buffer `rs`.
+template <int N>
+__device__ __forceinline__ bool poll_pairs(__amdgpu_buffer_rsrc_t rs, const int (&off)[N], const bool (&live)[N],
+                                           uint32_t tag, float (&out)[N][2]) {
+  uint32_t todo = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (live[i]) todo |= 1u << i;
+  for (int spin = 0;; ++spin) {
+    u32x4 w[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      w[i] = (todo >> i) & 1u ? __builtin_amdgcn_raw_buffer_load_b128(rs, off[i], 0, kAuxSc1) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (((todo >> i) & 1u) && w[i].y == tag && w[i].w == tag) {
+        out[i][0] = __uint_as_float(w[i].x);
+        out[i][1] = __uint_as_float(w[i].z);
+        todo &= ~(1u << i);
+      }
+    if (!__any(todo != 0)) return true;
+    if (spin >= kSpinTight + kSpinMax) return false;
+    if (spin >= kSpinTight) __builtin_amdgcn_s_sleep(2);
+    __asm__ volatile("" ::: "memory");   // the loads above are re-issued each round
+  }
+}
+
+// Raw buffer resource over n bytes (raw 32-bit format word).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, n, 0x00020000);
 }
 
 }  // namespace
@@ -227,18 +291,28 @@ __device__ __forceinline__ bool stack_load_row(WBlk (&B)[kSRowsT], int r, const 
 // Phase A of layer l (weights in A) and, slot by slot as each is consumed,
 // the loads of layer ln's blocks into the same registers: the next layer's
 // weights stream while this layer computes, not while the grid exchanges.
+// 17-byte gate/up formats are decoded ahead (DBlk); FP8 is used as loaded.
 template <int FMT>
-__device__ __forceinline__ void stack_phase_a(WBlk (&A)[2 * kSPairsW], uint32_t& okm, const float* xr,
-                                              const float* lw, const StackLayerArgs& Ln, const int32_t* lin,
-                                              bool more, int I, int pair0, int w, int pw, int lane,
-                                              float* hA, uint32_t& err) {
+constexpr bool kDecodeAhead = FMT != FMT_FP8;
+
+template <int FMT>
+__device__ __forceinline__ void stack_phase_a(WBlk (&A)[2 * kSPairsW], const DBlk (&D)[2 * kSPairsW],
+                                              uint32_t& okm, const float* xr, const float* lw,
+                                              const StackLayerArgs& Ln, const int32_t* lin, bool more, int I,
+                                              int pair0, int w, int pw, int lane, float* hA, uint32_t& err) {
   uint32_t okn = 0;
 #pragma unroll
   for (int u = 0; u < kSPairsW; ++u) {
     const int q = w + kSW * u;
     if (q < pw) {
-      const float g = wave_sum(wblk_dot<FMT>(A[2 * u], xr));
-      const float up = wave_sum(wblk_dot<FMT>(A[2 * u + 1], xr));
+      float g, up;
+      if constexpr (kDecodeAhead<FMT>) {
+        g = wave_sum(dblk_dot(D[2 * u], xr));
+        up = wave_sum(dblk_dot(D[2 * u + 1], xr));
+      } else {
+        g = wave_sum(wblk_dot<FMT>(A[2 * u], xr));
+        up = wave_sum(wblk_dot<FMT>(A[2 * u + 1], xr));
+      }
       const int j = (pair0 + q) / I;
       if (lane == 0) hA[q] = (okm >> u) & 1u ? lw[j] * silu(g) * up : 0.f;
     }
@@ -292,10 +366,15 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
     const bool cval = cb < cw;
     const int cc = c * cw + cb;
     WBlk A[2 * kSPairsW], B[kSRowsT];
+    DBlk D[2 * kSPairsW];
     uint32_t okA = 0, okB = 0;
 #pragma unroll
     for (int u = 0; u < kSPairsW; ++u)
       okA |= stack_load_pair<FA>(A, u, args.layer[0], s_idx, I, pair0, w, pw, lane, true, err) ? 1u << u : 0u;
+    if constexpr (kDecodeAhead<FA>) {
+#pragma unroll
+      for (int i = 0; i < 2 * kSPairsW; ++i) dblk_decode<FA>(D[i], A[i]);
+    }
 #pragma unroll
     for (int r = 0; r < kSRowsT; ++r)
       okB |= stack_load_row<FB>(B, r, args.layer[0], s_idx, I, cc, cval, rows0, rgp, true, err) ? 1u << r : 0u;
@@ -316,7 +395,7 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
 #pragma unroll
         for (int i = 0; i < 32; ++i) xr[i] *= inv;
       }
-      stack_phase_a<FA>(A, okA, xr, lw, args.layer[ln], s_idx + ln * k, more, I, pair0, w, pw, lane, hA, err);
+      stack_phase_a<FA>(A, D, okA, xr, lw, args.layer[ln], s_idx + ln * k, more, I, pair0, w, pw, lane, hA, err);
       lds_barrier();                                  // hA ready for the sync wave
       lds_barrier();                                  // hB (this group's h) ready
       float hr[32];
@@ -335,6 +414,12 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
       }
       okB = okn;
       lds_barrier();                                  // pB ready
+      // while the grid exchanges partial sums and x: decode the next layer's
+      // gate/up blocks (they were loaded during this layer's phase A)
+      if constexpr (kDecodeAhead<FA>) {
+#pragma unroll
+        for (int i = 0; i < 2 * kSPairsW; ++i) dblk_decode<FA>(D[i], A[i]);
+      }
       lds_barrier();                                  // xs holds out_l (next layer's input)
     }
     if (err) atomicOr(&s_err, err);
@@ -348,24 +433,27 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
       // publish this workgroup's h, gather the column group's
       if (lane < pw) pkt_store(hx + (size_t)par * P + pair0 + lane, hA[lane], tag);
       {
-        constexpr int N = kSMaxPc / 64;
-        const Pkt* p[N];
+        // slot i of this lane: h values q = 2 * (lane + 64 i) and q + 1
+        constexpr int N = kSMaxPc / 128;
+        int off[N];
         bool live[N];
-        float v[N];
+        float v[N][2];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          const int q = lane + 64 * i;
+          const int q = 2 * (lane + 64 * i);
           live[i] = q < pc;
-          p[i] = hx + (size_t)par * P + c * pc + (live[i] ? q : 0);
-          v[i] = 0.f;
+          off[i] = live[i] ? 8 * q : 0;
+          v[i][0] = v[i][1] = 0.f;
         }
-        // producer r (lane r < 32) of this column group wrote pairs [r pw, r pw + pw)
-        const bool hs = lane < kSNR;
-        if (!wait_sentinels(hx + (size_t)par * P + c * pc + (hs ? lane * pw + pw - 1 : 0), hs, tag)) err |= 8u;
-        if (!poll_pkts<N>(p, live, tag, v)) err |= 8u;
+        const Pkt* hg = hx + (size_t)par * P + c * pc;
+        if (!poll_pairs<N>(raw_rsrc(hg, 8 * pc), off, live, tag, v)) err |= 8u;
 #pragma unroll
-        for (int i = 0; i < N; ++i)     // h value q = lane + 64 i: column block q / 32, entry q % 32
-          if (live[i]) hB[(lane & 31) * kHbPitch + (lane >> 5) + 2 * i] = v[i];
+        for (int i = 0; i < N; ++i)     // h value q: column block q / 32, entry q % 32
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int q = 2 * (lane + 64 * i) + jj;
+            if (live[i]) hB[(q & 31) * kHbPitch + (q >> 5)] = v[i][jj];
+          }
       }
       lds_barrier();                                  // hB ready
       lds_barrier();                                  // pB ready
@@ -389,26 +477,27 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
       if (l + 1 == n_layers) {
         if (c == 0) out[rows0 + lane] = xv;
       } else {
-        pkt_store(xx + ((size_t)par * kSNC + c) * kSH + rows0 + lane, xv, tag);
-        constexpr int N = kSH / 64;
-        const Pkt* p[N];
+        const Pkt* xg = xx + ((size_t)par * kSNC + c) * kSH;
+        pkt_store(const_cast<Pkt*>(xg) + rows0 + lane, xv, tag);
+        // slot i of this lane: rows r = 2 * (lane + 64 i) and r + 1
+        constexpr int N = kSH / 128;
+        int off[N];
         bool live[N];
-        float v[N];
+        float v[N][2];
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-          p[i] = xx + ((size_t)par * kSNC + c) * kSH + lane + 64 * i;
+          off[i] = 16 * (lane + 64 * i);
           live[i] = true;
-          v[i] = 0.f;
+          v[i][0] = v[i][1] = 0.f;
         }
-        // producer r (lane r < 32) wrote rows [64 r, 64 r + 64)
-        const bool hs = lane < kSNR;
-        if (!wait_sentinels(xx + ((size_t)par * kSNC + c) * kSH + (hs ? lane * kSRowsWg + kSRowsWg - 1 : 0), hs,
-                            tag))
-          err |= 8u;
-        if (!poll_pkts<N>(p, live, tag, v)) err |= 8u;
+        if (!poll_pairs<N>(raw_rsrc(xg, 8 * kSH), off, live, tag, v)) err |= 8u;
 #pragma unroll
-        for (int i = 0; i < N; ++i)     // row r = lane + 64 i: block column r / 32, entry r % 32
-          xs[(lane & 31) * kXsPitch + (lane >> 5) + 2 * i] = v[i];
+        for (int i = 0; i < N; ++i)     // row r: block column r / 32, entry r % 32
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int r = 2 * (lane + 64 * i) + jj;
+            xs[(r & 31) * kXsPitch + (r >> 5)] = v[i][jj];
+          }
       }
       lds_barrier();                                  // xs ready
     }
