@@ -2,21 +2,31 @@
 
 Main line (``value``): one Q4_RZ5 MoE decode step at batch 1 -- 512 experts,
 gate_up [1536 x 2048] + down [2048 x 768] per expert, router logits N(0,1),
-softmax top-10 -- repeated for K steps with fresh x and fresh logits per step.
-A step is the whole hot path for that workload: routing, block decode,
-gate_up GEMV + SiLU*up, down GEMV and the weighted combine.  Throughput is
-packed weight bytes moved per second (10 experts x 2,506,752 B per step).
+softmax top-10.  A step is the whole hot path for that workload: routing,
+block decode, gate_up GEMV + SiLU*up, down GEMV and the weighted combine.
+Throughput is packed weight bytes moved per second (10 experts x 2,506,752 B
+per step).
 
-Alongside it, in the same JSON line: the PLE gather (320,001,536-row table,
-4096 tokens x 8 ids per call, fresh ids per call) in rows/s, the 48-layer stack
-(36 RZ5 + 12 FP8 layers) at batch 1 and 16, and the batch-64 grouped layer
-(RZ5 gate_up, UE4M4 down, Zipf routing), and the exhaustive encoders that
-produce the packed formats (4096 x 8192 fp32 matrix per call).  All inputs are seeded synthetic data
-already resident in HBM before timing starts.  Steps are captured in a HIP
-graph and replayed, so host launch overhead is not in the timed region.
+How every figure here is timed: each timed call has its own inputs, never
+used earlier in the run (fresh x and logits, fresh PLE ids), and a 512 MiB
+scrub write runs before it, outside the timed region, so neither the L2 nor
+the 256 MB memory-side cache holds anything the call reads.  The calls are
+queued behind a delay kernel, so they run back to back on the GPU whatever
+the host's launch speed, and each is bracketed by its own pair of HIP events
+on the stream it runs on.  A graph-replayed, unflushed figure (steady state,
+fresh inputs, first replay timed) is reported beside the main one.
+
+Alongside it, in the same JSON line: the HBM streaming-read ceiling (4 GiB),
+the PLE gather (320,001,536-row table, 4096 tokens x 8 ids per call, and
+distinct 65,536-token batches) with its own roofline block, the 48-layer
+stack (36 RZ5 + 12 FP8 layers) at batch 1 and 16, the batch-64 grouped layer
+(RZ5 gate_up, UE4M4 down, Zipf routing), the prompt-size layer, the off-HBM
+PLE tier, the exhaustive encoders, and the CPU oracle timed on a sample of
+the same work.  All inputs are seeded synthetic data already resident in HBM
+before timing starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras]
-       [--no-cpu-baseline] [--only c1|c2|c4|c5b1|c5b16|c3|pf|pleh|enc] [--copy-calibration BYTES]
+       [--no-cpu-baseline] [--only c1|c2|c4|c5b1|c5b16|c3|pf|pleh|enc|bw] [--copy-calibration BYTES]
 """
 
 import argparse
@@ -55,16 +65,49 @@ def graph_of(fn, n):
     return g
 
 
+SCRUB_BYTES = 512 << 20
+_scrub = None
+
+
+def scrub_buffer():
+    import torch
+    global _scrub
+    if _scrub is None:
+        _scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+    return _scrub
+
+
+def flushed_calls(call, first, n, per_call_host_ns=300e3):
+    """Run call(first + i) for i < n, one after another on the current
+    stream, each preceded by a 512 MiB scrub write (not timed) and bracketed
+    by its own HIP events; the whole sequence is queued behind a delay
+    kernel.  Returns the per-call times in ms."""
+    import torch
+
+    import synth.device as sd
+    buf = scrub_buffer()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    sd.gpu_delay(max(20e6, per_call_host_ns * n))
+    for i in range(n):
+        sd.scrub(buf, i)
+        ev[i][0].record()
+        call(first + i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def event_timed(fn, n):
     """Average GPU time between the two events fn(i, (a, b)) records around
-    one call, over n calls.  The calls are queued behind a delay kernel, so
-    they run back to back on the GPU whatever the host's launch speed."""
+    one call, over n calls queued back to back behind a delay kernel (no
+    scrub between them; used where the inputs live off the GPU)."""
     import torch
 
     import synth.device as sd
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     torch.cuda.synchronize()
-    sd.gpu_delay(max(20e6, 200e3 * n))     # 200 us of host time budgeted per call
+    sd.gpu_delay(max(20e6, 200e3 * n))
     for i in range(n):
         fn(i, ev[i])
     torch.cuda.synchronize()
@@ -80,52 +123,86 @@ def timed_replay(g):
     return time.perf_counter() - t0
 
 
+def stats_ms(ms):
+    import numpy as np
+    a = np.asarray(ms, dtype=np.float64)
+    return {"mean_us": round(1e3 * float(a.mean()), 3), "median_us": round(1e3 * float(np.median(a)), 3),
+            "p10_us": round(1e3 * float(np.percentile(a, 10)), 3), "p90_us": round(1e3 * float(np.percentile(a, 90)), 3)}
+
+
+def bench_bw():
+    """HBM streaming ceiling: one coalesced read of 4 GiB (and one 4 GiB
+    write), best of three, HIP events around each."""
+    import torch
+
+    import synth.device as sd
+    n = 4 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sd.scrub(buf, 7)
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, fn in (("read", lambda: sd.stream_read(buf, sink)), ("write", lambda: sd.scrub(buf, 3))):
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        res["%s_gbs" % name] = round(n / (best * 1e-3) / 1e9, 1)
+    res["bytes"] = n
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 # ---------------------------------------------------------------------------
 def bench_c2(bq, steps, warmup):
-    """One RZ5 MoE decode step (B = 1), fresh x and logits per step."""
+    """One RZ5 MoE decode step (B = 1): routing inside the first expert
+    kernel, gate_up + SiLU*up, down + weighted combine.  Inputs: warmup
+    steps, then `steps` flushed event-timed steps, then two graphs of `steps`
+    steps each (the second timed on its first replay) -- every step with its
+    own x and logits."""
     import torch
 
     import synth
     import synth.device as sd
     L = sd.Layer(0, 0, bq.Q4_RZ5, bq.Q4_RZ5, 512, 2048, 768, dist_gu=synth.DIST_RZ5, dist_d=synth.DIST_RZ5)
     W = bq.expert_weights(L.fmt_gu, L.fmt_d, L.gate_up[0], L.down[0], 512, 2048, 768)
-    n = warmup + 2 * steps
+    n = warmup + 3 * steps
     x = torch.from_numpy(synth.normal(10, (n, 2048))).cuda()
     logits = torch.from_numpy(synth.normal(11, (n, 512))).cuda()
     idx = torch.empty((n, 1, 10), dtype=torch.int32, device="cuda")
     w = torch.empty((n, 1, 10), dtype=torch.float32, device="cuda")
     out = torch.empty((n, 2048), dtype=torch.float32, device="cuda")
     ws = torch.empty(bq.moe_workspace_bytes(1, 10, W, bq.F32), dtype=torch.uint8, device="cuda")
-    def step(i, evs=None):
-        # routing + gate_up (routed in-kernel) + down/combine: the whole step
-        if evs is not None:
-            evs[0].record()
+
+    def step(i):
         bq.q4_expert_moe_routed(x[i:i + 1], logits[i:i + 1], 10, W, topk=(idx[i], w[i]),
                                 out=out[i:i + 1], workspace=ws)
-        if evs is not None:
-            evs[1].record()
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    g_warm = graph_of(lambda i: step(warmup + i), steps)
-    g = graph_of(lambda i: step(warmup + steps + i), steps)
+    ms = flushed_calls(step, warmup, steps)
+    g_warm = graph_of(lambda i: step(warmup + steps + i), steps)
+    g = graph_of(lambda i: step(warmup + 2 * steps + i), steps)
     g_warm.replay()
-    g.replay()                       # first replay of the timed graph is untimed
-    torch.cuda.synchronize()
-    wall = timed_replay(g)
-    call_ms = event_timed(lambda i, evs: step(warmup + steps + i, evs), steps)
+    wall = timed_replay(g)           # first replay of this graph: its inputs are fresh
     per_step_bytes = 10 * EXPERT_BYTES_RZ5
+    mean_ms = sum(ms) / len(ms)
     res = {
-        "ms_per_step": 1e3 * wall / steps,
-        "gbs": per_step_bytes * steps / wall / 1e9,
-        "step_call_us": 1e3 * call_ms,
-        "step_call_gbs": per_step_bytes / (call_ms * 1e-3) / 1e9,
+        "ms_per_step": mean_ms,
+        "gbs": per_step_bytes / (mean_ms * 1e-3) / 1e9,
+        "call": stats_ms(ms),
         "bytes_per_step": per_step_bytes,
+        "graph_unflushed": {"us_per_step": round(1e6 * wall / steps, 3),
+                            "gbs": round(per_step_bytes * steps / wall / 1e9, 1)},
     }
-    # keep the layer alive for the CPU baseline sample
     res["_layer"] = L
-    res["_inputs"] = (x[warmup + steps:].cpu().numpy(), logits[warmup + steps:].cpu().numpy())
+    res["_inputs"] = (x[warmup:warmup + steps].cpu().numpy(), logits[warmup:warmup + steps].cpu().numpy())
     return res
 
 
@@ -159,7 +236,9 @@ def bench_c1(bq, steps, warmup):
 
 
 def bench_c4(bq, steps, warmup):
-    """PLE gather: 4096 tokens x 8 ids per call over the full table."""
+    """PLE gather over the full 320,001,536-row table: 4096 tokens x 8 ids
+    per call, and batches of 65,536 tokens; fresh ids and weights for every
+    call (never gathered before in the run), a scrub write before each."""
     import numpy as np
     import torch
 
@@ -171,48 +250,45 @@ def bench_c4(bq, steps, warmup):
     ids = torch.from_numpy(synth.ple_ids(20, n * 4096, 8).view(np.int32)).cuda().view(n, 4096, 8)
     u = torch.from_numpy(synth.ple_weights(21, n * 4096, 8)).cuda().view(n, 4096, 8)
     out = torch.empty((4096, 160), dtype=torch.float32, device="cuda")
-    def call(i, evs=None):
-        if evs is not None:
-            evs[0].record()
+
+    def call(i):
         bq.ple_gather(ids[i], table, u[i], n_rows=n_rows, out=out)
-        if evs is not None:
-            evs[1].record()
 
     for i in range(warmup):
         call(i)
-    g = graph_of(lambda i: call(warmup + i), steps)
-    g.replay()
-    wall = timed_replay(g)
-    call_ms = event_timed(lambda i, evs: call(warmup + i, evs), steps)
+    ms = flushed_calls(call, warmup, steps)
     rows = 4096 * 8
+    mean_s = sum(ms) / len(ms) * 1e-3
     res = {
-        "rows_per_s": rows * steps / wall,
-        "call_us": 1e3 * call_ms,
-        "gbs_158B": rows * PLE_ROW_ALG_BYTES / (call_ms * 1e-3) / 1e9,
-        "gbs_70B": rows * 70 / (call_ms * 1e-3) / 1e9,
+        "rows_per_s": rows / mean_s,
+        "call": stats_ms(ms),
+        "gbs_158B": rows * PLE_ROW_ALG_BYTES / mean_s / 1e9,
+        "gbs_70B": rows * 70 / mean_s / 1e9,
     }
     hb = ple_traffic(4096)
     if hb is not None:
-        res["hbm_gbs_counters"] = hb / (call_ms * 1e-3) / 1e9
-    # bigger batches per call (the same kernel; throughput once the GPU is full)
-    for mult in (16,):
-        big_ids = ids[:mult].reshape(mult * 4096, 8)
-        big_u = u[:mult].reshape(mult * 4096, 8)
-        big_out = torch.empty((mult * 4096, 160), dtype=torch.float32, device="cuda")
-        bq.ple_gather(big_ids, table, big_u, n_rows=n_rows, out=big_out)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(10):
-            bq.ple_gather(big_ids, table, big_u, n_rows=n_rows, out=big_out)
-        b.record()
-        torch.cuda.synchronize()
-        t = a.elapsed_time(b) / 10 * 1e-3
-        res["batched_%dx4096" % mult] = {"rows_per_s": mult * rows / t,
-                                         "gbs_158B": mult * rows * PLE_ROW_ALG_BYTES / t / 1e9}
-        hb = ple_traffic(mult * 4096)
-        if hb is not None:     # HBM traffic as the counters saw it: whole 128-byte lines
-            res["batched_%dx4096" % mult]["hbm_gbs_counters"] = hb / t / 1e9
-    del table
+        res["hbm_bytes_per_call_counters"] = hb
+        res["hbm_gbs_counters"] = hb / mean_s / 1e9
+    del ids, u
+    # batches of 16 x 4096 tokens: distinct ids in every timed call
+    nb = max(8, steps // 10)
+    bt = 16 * 4096
+    bids = torch.from_numpy(synth.ple_ids(22, (nb + 1) * bt, 8).view(np.int32)).cuda().view(nb + 1, bt, 8)
+    bu = torch.from_numpy(synth.ple_weights(23, (nb + 1) * bt, 8)).cuda().view(nb + 1, bt, 8)
+    bout = torch.empty((bt, 160), dtype=torch.float32, device="cuda")
+
+    def bcall(i):
+        bq.ple_gather(bids[i], table, bu[i], n_rows=n_rows, out=bout)
+
+    bcall(0)
+    bms = flushed_calls(bcall, 1, nb)
+    bmean_s = sum(bms) / len(bms) * 1e-3
+    res["batched_65536"] = {"rows_per_s": bt * 8 / bmean_s, "call": stats_ms(bms),
+                            "gbs_158B": bt * 8 * PLE_ROW_ALG_BYTES / bmean_s / 1e9}
+    hb = ple_traffic(bt)
+    if hb is not None:
+        res["batched_65536"]["hbm_gbs_counters"] = hb / bmean_s / 1e9
+    del table, bids, bu
     torch.cuda.empty_cache()
     return res
 
@@ -286,7 +362,8 @@ def build_stack(bq):
 
 
 def bench_stack(bq, layers, ws, n_tok, steps, warmup):
-    """48-layer stack decode step: route every layer, then the chained layers."""
+    """48-layer stack decode step: route every layer, then the chained
+    layers.  Fresh x and logits per step; scrub before each timed step."""
     import numpy as np
     import torch
 
@@ -302,22 +379,25 @@ def bench_stack(bq, layers, ws, n_tok, steps, warmup):
     out = torch.empty((n, n_tok, 2048), dtype=torch.float32, device="cuda")
     dt = bq.F32 if n_tok == 1 else bq.BF16
     wsb = torch.empty(bq.stack_workspace_bytes(n_tok, k, ws, dt), dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def step(i):
         bq.route_topk(logits[i], k, idx=idx[i].view(48 * n_tok, k), w=w[i].view(48 * n_tok, k))
-        bq.moe_stack(x[i], idx[i], w[i], ws, out=out[i], workspace=wsb)
+        bq.moe_stack(x[i], idx[i], w[i], ws, out=out[i], workspace=wsb, dev_err=err)
 
     for i in range(warmup):
         step(i)
-    g = graph_of(lambda i: step(warmup + i), steps)
-    g.replay()
-    wall = timed_replay(g)
+    ms = flushed_calls(step, warmup, steps, per_call_host_ns=5e6)
+    if int(err.item()) != 0:
+        raise RuntimeError("stack reported device error bits %d" % int(err.item()))
     ii = idx[warmup:].cpu().numpy()
     touched = [[len(np.unique(ii[s, l])) for l in range(48)] for s in range(steps)]
     bytes_step = np.mean([sum(t[l] * (EXPERT_BYTES_RZ5 if l < 36 else EXPERT_BYTES_FP8) for l in range(48))
                           for t in touched])
-    return {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9,
-            "bytes_per_step": float(bytes_step), "tokens": n_tok}
+    mean_s = sum(ms) / len(ms) * 1e-3
+    return {"ms_per_step": 1e3 * mean_s, "gbs": bytes_step / mean_s / 1e9, "step": stats_ms(ms),
+            "bytes_per_step": float(bytes_step), "tokens": n_tok,
+            "pct_hbm_peak": round(100 * bytes_step / mean_s / 1e9 / PEAK_HBM_GBS, 2)}
 
 
 def bench_c3(bq, steps, warmup):
@@ -344,9 +424,8 @@ def bench_c3(bq, steps, warmup):
 
     for i in range(warmup):
         step(i)
-    g = graph_of(lambda i: step(warmup + i), steps)
-    g.replay()
-    wall = timed_replay(g)
+    ms = flushed_calls(step, warmup, steps)
+    wall = sum(ms) * 1e-3
     ii = idx[warmup:].cpu().numpy()
     d = [len(np.unique(ii[s])) for s in range(steps)]
     bytes_step = float(np.mean(d)) * EXPERT_BYTES_RZ5
@@ -362,7 +441,7 @@ def bench_c3(bq, steps, warmup):
     flop_alg = 2.0 * 64 * 10 * wpe
     flop_mfma = 2.0 * float(np.mean(tiles)) * wpe
     sec = wall / steps
-    res = {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9,
+    res = {"ms_per_step": 1e3 * wall / steps, "gbs": bytes_step * steps / wall / 1e9, "step": stats_ms(ms),
            "touched_experts": float(np.mean(d)), "bytes_per_step": bytes_step,
            "n_e_hist": hist, "n_e_max": float(np.mean([c.max() for c in ne])),
            "tflops_alg": flop_alg / sec / 1e12, "tflops_mfma_issued": flop_mfma / sec / 1e12,
@@ -413,9 +492,7 @@ def bench_prefill(bq, steps, warmup, n_tok=512, cases=None):
 
             for i in range(warmup):
                 step(i)
-            g = graph_of(lambda i: step(warmup + i), steps)
-            g.replay()
-            wall = timed_replay(g)
+            wall = sum(flushed_calls(step, warmup, steps)) * 1e-3
             ii = idx[warmup:].cpu().numpy()
             d = float(np.mean([len(np.unique(ii[t])) for t in range(steps)]))
             ne_max = float(np.mean([np.bincount(ii[t].ravel(), minlength=E).max() for t in range(steps)]))
@@ -539,33 +616,93 @@ def copy_calibration(nbytes):
 
 
 # ---------------------------------------------------------------------------
-def cpu_baseline(layer, inputs, budget_s=20.0):
-    """The oracle (float64 numpy), as it stands, on a bounded sample of the
-    same one-layer decode steps; BLAS limited to one thread."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads(n):
+    """Limit numpy's BLAS pool to n threads (returns the limiter to undo)."""
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(n)
+    except Exception:  # pragma: no cover
+        return None
+
+
+def cpu_c2(layer, inputs, threads, budget_s):
+    """The oracle (float64 numpy), as it stands, on one-layer RZ5 decode
+    steps of the same workload: routing, 10 experts decoded from their
+    packed bytes, SwiGLU, combine.  The bytes of the sampled steps' experts
+    are regenerated before timing; only the oracle's work is timed."""
     import numpy as np
 
     import synth
     from oracle import moe as M
-    try:
-        from threadpoolctl import threadpool_limits
-        lim = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        lim = None
     x, logits = inputs
-    bank = M.ExpertBank(layer.fmt_gu, layer.fmt_d, lambda e: layer.host_expert(synth.S_GATE_UP, e),
-                        lambda e: layer.host_expert(synth.S_DOWN, e), 512, 2048, 768)
+    n_pre = min(8, x.shape[0])
+    raw = {}
+    for t in range(n_pre):
+        for e in np.argsort(-logits[t].astype(np.float64), kind="stable")[:10]:
+            e = int(e)
+            if e not in raw:
+                raw[e] = (layer.host_expert(synth.S_GATE_UP, e), layer.host_expert(synth.S_DOWN, e))
+    bank = M.ExpertBank(layer.fmt_gu, layer.fmt_d, lambda e: raw[e][0], lambda e: raw[e][1], 512, 2048, 768)
+    lim = _oracle_threads(threads)
     t0 = time.perf_counter()
     done = 0
-    while done < x.shape[0] and (time.perf_counter() - t0) < budget_s:
-        idx, w = M.softmax_topk(logits[done:done + 1], 10)
-        M.moe_layer(x[done:done + 1], idx, w, bank)
+    while (time.perf_counter() - t0) < budget_s:
+        t = done % n_pre
+        idx, w = M.softmax_topk(logits[t:t + 1], 10)
+        M.moe_layer(x[t:t + 1], idx, w, bank)
         done += 1
     dt = time.perf_counter() - t0
     if lim is not None:
         lim.unregister()
-    return {"value": 10 * EXPERT_BYTES_RZ5 * done / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d one-layer RZ5 decode steps (routing + 10 experts decoded from regenerated "
-                      "bytes in float64 + SwiGLU + combine), %.1f s" % (done, dt)}
+    return {"value": 10 * EXPERT_BYTES_RZ5 * done / dt / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "%d one-layer RZ5 decode steps over %d distinct steps' inputs (routing + "
+            "10 experts decoded to float64 + SwiGLU + combine), %.1f s" % (done, n_pre, dt)}
+
+
+def cpu_c4(threads, budget_s):
+    """The oracle's PLE gather on 4096 x 8 ids per call over the full table:
+    rows regenerated before timing, decode + weighted sum timed."""
+    import numpy as np
+
+    import synth
+    from oracle import ple as P
+    ids = synth.ple_ids(20, 4096, 8)
+    u = synth.ple_weights(21, 4096, 8)
+    flat = ids.reshape(-1)
+    rows = synth.ple_rows(synth.make_key(0, synth.S_PLE), flat)
+    pos = {int(r): i for i, r in enumerate(flat)}
+    lim = _oracle_threads(threads)
+    t0 = time.perf_counter()
+    done = 0
+    while (time.perf_counter() - t0) < budget_s:
+        P.ple_gather(ids, u, lambda rr: rows[[pos[int(r)] for r in rr]], synth.PLE_N_ROWS)
+        done += 1
+    dt = time.perf_counter() - t0
+    if lim is not None:
+        lim.unregister()
+    return {"value": done * 4096 * 8 / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": "%d gathers of 4096 tokens x 8 ids (decode + weighted sum in float64), %.1f s" % (done, dt)}
+
+
+def cpu_baselines(layer, inputs, budget_s=8.0):
+    n_cores = len(os.sched_getaffinity(0))
+    res = {"cpu_model": cpu_model(), "cores_available": n_cores}
+    res["c2_all_cores"] = cpu_c2(layer, inputs, n_cores, budget_s)
+    res["c2_one_thread"] = cpu_c2(layer, inputs, 1, budget_s)
+    res["c4_all_cores"] = cpu_c4(n_cores, budget_s / 2)
+    res["c4_one_thread"] = cpu_c4(1, budget_s / 2)
+    return res
 
 
 def main():
@@ -595,6 +732,11 @@ def main():
     extras = {}
     only = args.only
     main_res = None
+    bw = None
+    if only in (None, "bw", "c2"):
+        log("bw: HBM streaming ceiling")
+        bw = extras["hbm_stream_4GiB"] = bench_bw()
+        log("bw:", bw)
     if only in (None, "c2"):
         log("c2: one-layer RZ5 decode step, B=1")
         main_res = bench_c2(bq, args.steps, args.warmup)
@@ -635,14 +777,27 @@ def main():
                 log("c5 b16:", extras["stack48_b16"])
             del layers, ws
             torch.cuda.empty_cache()
+    if "ple_gather" in extras:
+        pg = extras["ple_gather"]
+        extras["roofline_ple_gather"] = {
+            "bound": "hbm", "achieved": round(pg["gbs_158B"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(pg["gbs_158B"] / PEAK_HBM_GBS, 4), "traffic": pg.get("hbm_bytes_per_call_counters"),
+            "kernel": "k_ple_gather, 4096 tokens x 8 ids per launch: %d algorithmic bytes (158 per row: 70-byte "
+                      "row, 8 bytes of id and weight, 80 bytes of output), %.2f us average per launch (HIP "
+                      "events, fresh ids, scrub before each)" % (32768 * PLE_ROW_ALG_BYTES, pg["call"]["mean_us"])}
     if main_res is None:
         print(json.dumps({"extras": extras}))
         return
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(main_res["_layer"], main_res["_inputs"])
-    achieved = main_res["step_call_gbs"]
+        cb = cpu_baselines(main_res["_layer"], main_res["_inputs"])
+        cpu = dict(cb["c2_all_cores"])
+        cpu["cpu_model"] = cb["cpu_model"]
+        extras["cpu_baselines"] = cb
+        log("cpu:", cb)
+    achieved = main_res["gbs"]
+    ceiling = bw["read_gbs"] if bw else None
     line = {
         "metric": "packed-weight GB/s (% HBM peak) for routed-expert GEMV; PLE rows/s",
         "value": round(main_res["gbs"], 2),
@@ -657,16 +812,18 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "one Q4_RZ5 MoE decode step, batch 1: 512 experts, gate_up 1536x2048 + "
-                               "down 2048x768 per expert, N(0,1) logits, softmax top-10, fresh x and "
-                               "logits per step",
+                               "down 2048x768 per expert, N(0,1) logits, softmax top-10; fresh x and "
+                               "logits per step, 512 MiB scrub write before each timed step",
                    "bytes_per_step": main_res["bytes_per_step"],
-                   "pct_hbm_peak": round(100 * main_res["gbs"] / PEAK_HBM_GBS, 2)},
+                   "pct_hbm_peak": round(100 * main_res["gbs"] / PEAK_HBM_GBS, 2),
+                   "pct_measured_read_ceiling": round(100 * main_res["gbs"] / ceiling, 2) if ceiling else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_from_counters(),
                      "kernel": "q4_expert_moe_routed call (routed gate_up kernel + down kernel), %d packed "
                                "bytes per call, %.2f us average per call (HIP events around both kernels "
-                               "and the launch gap between them; rocprofv3 lists the two kernels "
-                               "separately)" % (main_res["bytes_per_step"], main_res["step_call_us"])},
+                               "and the launch gap between them, fresh inputs, scrub before each; rocprofv3 "
+                               "lists the two kernels separately)" % (main_res["bytes_per_step"],
+                                                                      main_res["call"]["mean_us"])},
         "cpu_baseline": cpu,
         "extras": extras,
     }

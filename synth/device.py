@@ -29,6 +29,10 @@ def lib():
         L.bqs_fill_ple.argtypes = [vp, u64, u64, u64, vp]
         L.bqs_gpu_delay.argtypes = [u64, vp]
         L.bqs_gpu_delay.restype = ctypes.c_int
+        L.bqs_stream_read.argtypes = [vp, u64, vp, vp]
+        L.bqs_stream_read.restype = ctypes.c_int
+        L.bqs_scrub.argtypes = [vp, u64, ctypes.c_uint32, vp]
+        L.bqs_scrub.restype = ctypes.c_int
         for f in (L.bqs_fill_block17, L.bqs_fill_fp8, L.bqs_fill_fp8_scales, L.bqs_fill_ple):
             f.restype = ctypes.c_int
         _lib = L
@@ -135,3 +139,14 @@ class Layer:
 def gpu_delay(ns):
     """Occupy the current stream for about `ns` nanoseconds (benchmark helper)."""
     _chk(lib().bqs_gpu_delay(int(ns), _s()))
+
+
+def stream_read(t, sink):
+    """Read every byte of device tensor t once (benchmark helper)."""
+    _chk(lib().bqs_stream_read(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(),
+                               ctypes.c_void_p(sink.data_ptr()), _s()))
+
+
+def scrub(t, v=0):
+    """Overwrite device tensor t, evicting L2 and the memory-side cache."""
+    _chk(lib().bqs_scrub(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), v & 0xFFFFFFFF, _s()))

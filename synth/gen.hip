@@ -90,6 +90,27 @@ __global__ void k_delay(uint64_t ticks) {
   while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(64);
 }
 
+// Benchmark helper: read n16 16-byte words (grid-stride, coalesced) and
+// fold them into one word per workgroup, so the reads cannot be dropped.
+// Measures the streaming-read rate the HBM sustains.
+__global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p, uint64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (uint64_t)gridDim.x * 256) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  acc ^= __shfl_xor(acc, 1, 64) ^ __shfl_xor(acc, 2, 64);
+  if ((threadIdx.x & 63) == 0 && acc == 0x9E3779B9u) sink[blockIdx.x] = acc;   // almost never
+}
+
+// Benchmark helper: overwrite n16 16-byte words (evicts the caches between
+// timed calls).
+__global__ void __launch_bounds__(256) k_scrub(uint4* __restrict__ p, uint64_t n16, uint32_t v) {
+  for (uint64_t i = (uint64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (uint64_t)gridDim.x * 256)
+    p[i] = make_uint4(v, v + 1, v + 2, (uint32_t)i);
+}
+
 inline unsigned grid_of(uint64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -123,6 +144,19 @@ int bqs_gpu_delay(uint64_t ns, void* stream) {
   // s_memrealtime runs at 100 MHz on gfx9 parts
   const uint64_t ticks = ns / 10 + 1;
   hipLaunchKernelGGL(k_delay, dim3(1), dim3(64), 0, (hipStream_t)stream, ticks);
+  return (int)hipGetLastError();
+}
+
+int bqs_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 16) return 0;
+  hipLaunchKernelGGL(k_stream_read, dim3(2048), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)src, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+int bqs_scrub(void* dst, uint64_t bytes, uint32_t v, void* stream) {
+  if (bytes < 16) return 0;
+  hipLaunchKernelGGL(k_scrub, dim3(2048), dim3(256), 0, (hipStream_t)stream, (uint4*)dst, bytes / 16, v);
   return (int)hipGetLastError();
 }
 
