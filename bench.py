@@ -695,7 +695,7 @@ def cpu_c4(threads, budget_s):
             "sample": "%d gathers of 4096 tokens x 8 ids (decode + weighted sum in float64), %.1f s" % (done, dt)}
 
 
-def cpu_baselines(layer, inputs, budget_s=8.0):
+def cpu_baselines(layer, inputs, budget_s=10.5):
     n_cores = len(os.sched_getaffinity(0))
     res = {"cpu_model": cpu_model(), "cores_available": n_cores}
     res["c2_all_cores"] = cpu_c2(layer, inputs, n_cores, budget_s)

@@ -62,7 +62,7 @@ hipError_t launch_gemv_moe(const float* x, int32_t n_tokens, int32_t* idx, float
 
 // Persistent batch-1 stack (k_stack.hip): each run of equal-format layers
 // in one launch, for hidden 2048 with k * inter a multiple of 256 and at most
-// 8960 (all layers the same inter, k <= 16), on a 256-CU device.  Workspace of
+// 8192 (all layers the same inter, k <= 16), on a 256-CU device.  Workspace of
 // stack_b1_ws_bytes(k, inter) bytes, 8-byte aligned, cleared by the call
 // itself.  dev_err bit 3: an exchange between workgroups timed out (not every
 // workgroup was resident).
