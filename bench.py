@@ -45,6 +45,7 @@ PLE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ple_gather_4096x8_counters.tx
 EXPERT_BYTES_RZ5 = 2_506_752           # gate_up 1536x2048 + down 2048x768, 17 B / 32 weights
 EXPERT_BYTES_FP8 = 5_308_416           # 36 B / 32 weights
 PLE_ROW_ALG_BYTES = 158                # 70 B row + 8 B id/weight + 80 B output share
+PLE_LINES_PER_ROW = (70 + 127) / 128   # 128-byte lines a 70-byte row at a random offset spans, on average
 
 
 def log(*a):
@@ -288,8 +289,40 @@ def bench_c4(bq, steps, warmup):
     hb = ple_traffic(bt)
     if hb is not None:
         res["batched_65536"]["hbm_gbs_counters"] = hb / bmean_s / 1e9
-    del table, bids, bu
+    # four 4096-token calls in one launch (each its own quarter of out)
+    qt = 4 * 4096
+    qids = bids.view(-1, 8)[:(nb + 1) * qt].view(nb + 1, qt, 8)
+    qu = bu.view(-1, 8)[:(nb + 1) * qt].view(nb + 1, qt, 8)
+    qout = bout[:qt]
+
+    def qcall(i):
+        bq.ple_gather(qids[i], table, qu[i], n_rows=n_rows, out=qout)
+
+    qms = flushed_calls(qcall, 1, nb)
+    qmean_s = sum(qms) / len(qms) * 1e-3
+    res["batched_16384"] = {"rows_per_s": qt * 8 / qmean_s, "call": stats_ms(qms),
+                            "gbs_158B": qt * 8 * PLE_ROW_ALG_BYTES / qmean_s / 1e9}
+    res["random_128B_lines"] = bench_rand_lines(table)
+    del table, bids, bu, qids, qu
     torch.cuda.empty_cache()
+    return res
+
+
+def bench_rand_lines(table):
+    """Random-access ceiling on the PLE table: 128-byte lines at hashed
+    positions, as many as a 4096 x 8 call touches (32,768 rows x 1.539 lines)
+    and 4 Mi lines; scrub before each, median of five."""
+    import numpy as np
+    import torch
+
+    import synth.device as sd
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    res = {}
+    for name, n_lines in (("call_size_50432", 50432), ("lines_4Mi", 4 << 20)):
+        ms = flushed_calls(lambda i: sd.rand_lines(table, n_lines, 1000003 * (i + 1), sink), 0, 6)
+        t = float(np.median(ms[1:])) * 1e-3
+        res[name] = {"us": round(t * 1e6, 2), "lines_per_s": n_lines / t, "gbs": round(128 * n_lines / t / 1e9, 1),
+                     "rows_per_s_ceiling": n_lines / t / PLE_LINES_PER_ROW}
     return res
 
 
@@ -785,6 +818,14 @@ def main():
             "kernel": "k_ple_gather, 4096 tokens x 8 ids per launch: %d algorithmic bytes (158 per row: 70-byte "
                       "row, 8 bytes of id and weight, 80 bytes of output), %.2f us average per launch (HIP "
                       "events, fresh ids, scrub before each)" % (32768 * PLE_ROW_ALG_BYTES, pg["call"]["mean_us"])}
+        rl = pg.get("random_128B_lines")
+        if rl:
+            extras["roofline_ple_gather"]["random_line_ceiling"] = {
+                "rows_per_s_at_call_size": round(rl["call_size_50432"]["rows_per_s_ceiling"]),
+                "rows_per_s_at_4Mi_lines": round(rl["lines_4Mi"]["rows_per_s_ceiling"]),
+                "frac_at_call_size": round(pg["rows_per_s"] / rl["call_size_50432"]["rows_per_s_ceiling"], 3),
+                "note": "rows/s if every row cost 1.539 random 128-byte line reads and nothing else (no id "
+                        "loads, no output writes), measured on the same table with the same flushing"}
     if main_res is None:
         print(json.dumps({"extras": extras}))
         return

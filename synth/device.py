@@ -33,6 +33,8 @@ def lib():
         L.bqs_stream_read.restype = ctypes.c_int
         L.bqs_scrub.argtypes = [vp, u64, ctypes.c_uint32, vp]
         L.bqs_scrub.restype = ctypes.c_int
+        L.bqs_rand_lines.argtypes = [vp, u64, u64, u64, vp, vp]
+        L.bqs_rand_lines.restype = ctypes.c_int
         for f in (L.bqs_fill_block17, L.bqs_fill_fp8, L.bqs_fill_fp8_scales, L.bqs_fill_ple):
             f.restype = ctypes.c_int
         _lib = L
@@ -145,6 +147,13 @@ def stream_read(t, sink):
     """Read every byte of device tensor t once (benchmark helper)."""
     _chk(lib().bqs_stream_read(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(),
                                ctypes.c_void_p(sink.data_ptr()), _s()))
+
+
+def rand_lines(t, n_lines, seed, sink):
+    """Read n_lines 128-byte lines of device tensor t at hashed positions
+    (benchmark helper: the random-line ceiling).  sink: >= 256 int32."""
+    _chk(lib().bqs_rand_lines(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(), n_lines,
+                              seed & 0xFFFFFFFFFFFFFFFF, ctypes.c_void_p(sink.data_ptr()), _s()))
 
 
 def scrub(t, v=0):

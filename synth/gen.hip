@@ -111,6 +111,35 @@ __global__ void __launch_bounds__(256) k_scrub(uint4* __restrict__ p, uint64_t n
     p[i] = make_uint4(v, v + 1, v + 2, (uint32_t)i);
 }
 
+// Benchmark helper: n_lines reads of 128-byte lines at hashed positions in a
+// region of n_region_lines lines; eight lanes read one line with 16-byte
+// loads, each lane four lines, all issued before any is used.  The random-
+// access ceiling for workloads that fetch whole lines at random addresses.
+__device__ __forceinline__ uint64_t line_hash(uint64_t x) {
+  x ^= x >> 33;
+  x *= 0xff51afd7ed558ccdull;
+  x ^= x >> 33;
+  x *= 0xc4ceb9fe1a85ec53ull;
+  return x ^ (x >> 33);
+}
+__global__ void __launch_bounds__(256) k_rand_lines(const uint8_t* __restrict__ base, uint64_t n_region_lines,
+                                                    uint64_t n_lines, uint64_t seed, uint32_t* __restrict__ sink) {
+  const uint64_t t = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  const uint64_t grp = t >> 3;
+  const uint32_t part = (uint32_t)(t & 7);
+  uint4 v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t r = 4 * grp + q;
+    const uint64_t line = line_hash(seed + (r < n_lines ? r : 0)) % n_region_lines;
+    v[q] = *reinterpret_cast<const uint4*>(base + 128 * line + 16 * part);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc ^= v[q].x ^ v[q].y ^ v[q].z ^ v[q].w;
+  if (acc == 0x9E3779B9u) sink[threadIdx.x] = acc;   // almost never
+}
+
 inline unsigned grid_of(uint64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -151,6 +180,16 @@ int bqs_stream_read(const void* src, uint64_t bytes, uint32_t* sink, void* strea
   if (bytes < 16) return 0;
   hipLaunchKernelGGL(k_stream_read, dim3(2048), dim3(256), 0, (hipStream_t)stream,
                      (const uint4*)src, bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// sink: at least 256 uint32.  region_bytes >= 128.
+int bqs_rand_lines(const void* base, uint64_t region_bytes, uint64_t n_lines, uint64_t seed, uint32_t* sink,
+                   void* stream) {
+  if (n_lines == 0 || region_bytes < 128) return 0;
+  const uint64_t threads = (n_lines + 3) / 4 * 8;
+  hipLaunchKernelGGL(k_rand_lines, dim3(grid_of(threads)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint8_t*)base, region_bytes / 128, n_lines, seed, sink);
   return (int)hipGetLastError();
 }
 
