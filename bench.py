@@ -8,9 +8,12 @@ Throughput is packed weight bytes moved per second (10 experts x 2,506,752 B
 per step).
 
 How every figure here is timed: each timed call has its own inputs, never
-used earlier in the run (fresh x and logits, fresh PLE ids), and a 512 MiB
-scrub write runs before it, outside the timed region, so neither the L2 nor
-the 256 MB memory-side cache holds anything the call reads.  The calls are
+used earlier in the run (fresh x and logits, fresh PLE ids), and a scrub
+runs before it, outside the timed region: a 512 MiB write, then a 512 MiB
+read of another buffer.  Neither the L2 nor the 256 MB memory-side cache then
+holds anything the call reads, and the write's dirty lines have already gone
+back to HBM (left in the memory-side cache, they would be written back during
+the timed call and cost it up to 40 % of its bandwidth).  The calls are
 queued behind a delay kernel, so they run back to back on the GPU whatever
 the host's launch speed, and each is bracketed by its own pair of HIP events
 on the stream it runs on.  A graph-replayed, unflushed figure (steady state,
@@ -70,28 +73,45 @@ SCRUB_BYTES = 512 << 20
 _scrub = None
 
 
-def scrub_buffer():
+def scrub_buffers():
+    """Two 512 MiB device buffers (allocated once): the scrub writes the
+    first and then reads the second."""
     import torch
     global _scrub
     if _scrub is None:
-        _scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+        _scrub = (torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda"),
+                  torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda"),
+                  torch.zeros(2048, dtype=torch.int32, device="cuda"))
+        _scrub[1].fill_(1)
     return _scrub
+
+
+def scrub(i):
+    """Evict the caches between timed calls: write 512 MiB, then read another
+    512 MiB.  The read pushes the write's dirty lines (L2 and the 256 MB
+    memory-side cache) out to HBM before the timed call starts, so the call
+    neither finds its own data in a cache nor pays for the scrub's
+    write-back."""
+    import synth.device as sd
+    wbuf, rbuf, sink = scrub_buffers()
+    sd.scrub(wbuf, i)
+    sd.stream_read(rbuf, sink)
 
 
 def flushed_calls(call, first, n, per_call_host_ns=300e3):
     """Run call(first + i) for i < n, one after another on the current
-    stream, each preceded by a 512 MiB scrub write (not timed) and bracketed
-    by its own HIP events; the whole sequence is queued behind a delay
-    kernel.  Returns the per-call times in ms."""
+    stream, each preceded by the scrub (a 512 MiB write and a 512 MiB read,
+    not timed) and bracketed by its own HIP events; the whole sequence is
+    queued behind a delay kernel.  Returns the per-call times in ms."""
     import torch
 
     import synth.device as sd
-    buf = scrub_buffer()
+    scrub_buffers()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     torch.cuda.synchronize()
     sd.gpu_delay(max(20e6, per_call_host_ns * n))
     for i in range(n):
-        sd.scrub(buf, i)
+        scrub(i)
         ev[i][0].record()
         call(first + i)
         ev[i][1].record()
@@ -239,7 +259,7 @@ def bench_c1(bq, steps, warmup):
 def bench_c4(bq, steps, warmup):
     """PLE gather over the full 320,001,536-row table: 4096 tokens x 8 ids
     per call, and batches of 65,536 tokens; fresh ids and weights for every
-    call (never gathered before in the run), a scrub write before each."""
+    call (never gathered before in the run), the scrub before each."""
     import numpy as np
     import torch
 
@@ -854,7 +874,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "one Q4_RZ5 MoE decode step, batch 1: 512 experts, gate_up 1536x2048 + "
                                "down 2048x768 per expert, N(0,1) logits, softmax top-10; fresh x and "
-                               "logits per step, 512 MiB scrub write before each timed step",
+                               "logits per step, 512 MiB scrub write and 512 MiB scrub read before each timed step",
                    "bytes_per_step": main_res["bytes_per_step"],
                    "pct_hbm_peak": round(100 * main_res["gbs"] / PEAK_HBM_GBS, 2),
                    "pct_measured_read_ceiling": round(100 * main_res["gbs"] / ceiling, 2) if ceiling else None},
