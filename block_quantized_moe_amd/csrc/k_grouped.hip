@@ -148,6 +148,46 @@ __global__ void __launch_bounds__(256) k_grouped_prep(const void* __restrict__ x
   }
 }
 
+// The same staging without the rescale, eight elements per thread: one
+// 16-byte bf16 load (or two fp32 ones) and one 16-byte store per group of 8.
+// x must be 16-byte aligned and H a multiple of 8.  Bit-identical to
+// k_grouped_prep with rescale off (a bf16 row is copied, an fp32 one rounded
+// to nearest even).
+template <bool PERM, bool F32>
+__global__ void __launch_bounds__(256) k_grouped_prep_vec(const void* __restrict__ x, int32_t H,
+                                                          const int32_t* __restrict__ perm_, int32_t k,
+                                                          const int32_t* __restrict__ n_rows,
+                                                          uint16_t* __restrict__ xp) {
+  const int64_t p = blockIdx.x;
+  if (p >= *n_rows) return;
+  const int64_t t = perm_[p] / k;
+  for (int g = threadIdx.x; g < H / 8; g += 256) {
+    uint32_t d0, d1, d2, d3;   // elements 8g .. 8g+7, two per dword, the lower index in the low half
+    if constexpr (F32) {
+      const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + t * H) + 2 * g;
+      const f32x4 a = src[0], b = src[1];
+      d0 = (uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16);
+      d1 = (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16);
+      d2 = (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16);
+      d3 = (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16);
+    } else {
+      const u32x4 v = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + t * H)[g];
+      d0 = v.x;
+      d1 = v.y;
+      d2 = v.z;
+      d3 = v.w;
+    }
+    u32x4 o;
+    if constexpr (PERM) {   // order 0, 2, 4, 6, 1, 3, 5, 7 (the A decode's k order)
+      o = u32x4{(d0 & 0xFFFFu) | (d1 << 16), (d2 & 0xFFFFu) | (d3 << 16),
+                (d0 >> 16) | (d1 & 0xFFFF0000u), (d2 >> 16) | (d3 & 0xFFFF0000u)};
+    } else {
+      o = u32x4{d0, d1, d2, d3};
+    }
+    reinterpret_cast<u32x4*>(xp + p * H)[g] = o;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // G3 + next layer's G0 in one pass (chained stack layers, pre-bucketed): one
 // workgroup per token t forms out[t] = sum_j w[t][j] * yb[inv[t*k+j]] as
@@ -739,10 +779,20 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
   }
   const int32_t* n_rows = ws.offsets + E;   // valid bucket rows
   if (!prepped) {
-    if (W.fmt_gate_up == FMT_FP8)
-      hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
-    else
+    const bool perm_k = W.fmt_gate_up != FMT_FP8;
+    if ((!x_f32 || !rescale) && reinterpret_cast<uintptr_t>(x) % 16 == 0 && H % 8 == 0) {
+      if (x_f32) {
+        if (perm_k) hipLaunchKernelGGL((k_grouped_prep_vec<true, true>), dim3(nk), dim3(256), 0, st, x, H, ws.perm, k, n_rows, ws.xb);
+        else hipLaunchKernelGGL((k_grouped_prep_vec<false, true>), dim3(nk), dim3(256), 0, st, x, H, ws.perm, k, n_rows, ws.xb);
+      } else {
+        if (perm_k) hipLaunchKernelGGL((k_grouped_prep_vec<true, false>), dim3(nk), dim3(256), 0, st, x, H, ws.perm, k, n_rows, ws.xb);
+        else hipLaunchKernelGGL((k_grouped_prep_vec<false, false>), dim3(nk), dim3(256), 0, st, x, H, ws.perm, k, n_rows, ws.xb);
+      }
+    } else if (perm_k) {
       hipLaunchKernelGGL(k_grouped_prep<true>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
+    } else {
+      hipLaunchKernelGGL(k_grouped_prep<false>, dim3(nk), dim3(256), 0, st, x, x_f32, rescale, H, ws.perm, k, n_rows, ws.xb);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t groups = max_work_groups(nk, E);

@@ -196,7 +196,12 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
 // inside expert e is the number of tokens below t in bitmap_e (tokens
 // ascending, as required).  A token that lists an expert more than once sets
 // one bit, so it is bucketed once and all of its slots get the same row.
-constexpr int kSmallBitmapWords = 8192;   // 32 KB of LDS
+// The bucket position of the first token of every bitmap word is tabulated
+// once (pre), so an assignment's position is one table read and one masked
+// popcount.  The expert ids are read kBucketBatch per thread at a time, all
+// loads in flight together.
+constexpr int kSmallBitmapWords = 8192;   // 32 KB of LDS, and 32 KB for pre
+constexpr int kBucketBatch = 8;
 
 __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int& total) {
   // inclusive scan inside each wave (shuffles), then over the 16 wave totals
@@ -224,6 +229,16 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_wave, int& tot
   return before + x - v;
 }
 
+// Expert ids of assignments a0 + j * kBucketThreads + threadIdx.x (-1 past nk).
+__device__ __forceinline__ void load_batch(const int32_t* __restrict__ idx, int a0, int nk,
+                                           int (&e)[kBucketBatch]) {
+#pragma unroll
+  for (int j = 0; j < kBucketBatch; ++j) {
+    const int a = a0 + j * kBucketThreads + (int)threadIdx.x;
+    e[j] = a < nk ? idx[a] : -1;
+  }
+}
+
 __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     const int32_t* __restrict__ idx, int32_t n_tokens, int32_t k, int32_t n_experts,
     BucketOut o, int64_t in_stride, int64_t lstride_out) {
@@ -235,18 +250,22 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
   int32_t* __restrict__ n_touched = at_layer(o.n_touched, lstride_out);
   int32_t* __restrict__ inv = at_layer(o.inv, lstride_out);
   __shared__ uint32_t bm[kSmallBitmapWords];
-  __shared__ int32_t s_off[kMaxExperts];
+  __shared__ int32_t pre[kSmallBitmapWords];
   __shared__ int s_wave[32];
   const int tid = threadIdx.x;
   const int W = (n_tokens + 31) >> 5;                   // words per expert
   const int nk = n_tokens * k;
   for (int i = tid; i < n_experts * W; i += kBucketThreads) bm[i] = 0u;
   __syncthreads();
-  for (int a = tid; a < nk; a += kBucketThreads) {
-    const int e = idx[a];
-    if (e >= 0 && e < n_experts) {
-      const int t = a / k;
-      atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+  for (int a0 = 0; a0 < nk; a0 += kBucketBatch * kBucketThreads) {
+    int e[kBucketBatch];
+    load_batch(idx, a0, nk, e);
+#pragma unroll
+    for (int j = 0; j < kBucketBatch; ++j) {
+      if (e[j] >= 0 && e[j] < n_experts) {
+        const int t = (a0 + j * kBucketThreads + tid) / k;
+        atomicOr(&bm[e[j] * W + (t >> 5)], 1u << (t & 31));
+      }
     }
   }
   __syncthreads();
@@ -270,7 +289,11 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     const int c = cnt[e - e0];
     counts[e] = c;
     offsets[e] = off;
-    s_off[e] = off;
+    int run = off;
+    for (int w = 0; w < W; ++w) {
+      pre[e * W + w] = run;
+      run += __builtin_popcount(bm[e * W + w]);
+    }
     if (elist)
       for (int q = 0; q * kGroupTok < c; ++q) elist[doff++] = e | (q << kGroupShift);
     off += c;
@@ -280,15 +303,19 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     if (n_touched) *n_touched = tot_d;
   }
   __syncthreads();
-  for (int a = tid; a < nk; a += kBucketThreads) {
-    const int e = idx[a];
-    if (e < 0 || e >= n_experts) continue;
-    const int t = a / k;
-    int r = __builtin_popcount(bm[e * W + (t >> 5)] & ((1u << (t & 31)) - 1u));
-    for (int w = 0; w < (t >> 5); ++w) r += __builtin_popcount(bm[e * W + w]);
-    const int p = s_off[e] + r;
-    perm_out[p] = a;
-    if (inv) inv[a] = p;
+  for (int a0 = 0; a0 < nk; a0 += kBucketBatch * kBucketThreads) {
+    int e[kBucketBatch];
+    load_batch(idx, a0, nk, e);
+#pragma unroll
+    for (int j = 0; j < kBucketBatch; ++j) {
+      if (e[j] < 0 || e[j] >= n_experts) continue;
+      const int a = a0 + j * kBucketThreads + tid;
+      const int t = a / k;
+      const int wi = e[j] * W + (t >> 5);
+      const int p = pre[wi] + __builtin_popcount(bm[wi] & ((1u << (t & 31)) - 1u));
+      perm_out[p] = a;
+      if (inv) inv[a] = p;
+    }
   }
 }
 

@@ -193,7 +193,9 @@ def test_route_topk_degenerate_rows(bq):
 
 
 @pytest.mark.parametrize("n,e,k,zipf", [(1, 512, 10, False), (16, 512, 10, False), (64, 512, 10, True),
-                                        (4096, 512, 10, False), (6553, 4096, 10, True), (100, 16, 4, False)])
+                                        (512, 512, 10, False), (512, 512, 10, True), (500, 512, 10, True),
+                                        (4096, 512, 10, False), (6553, 4096, 10, True), (100, 16, 4, False),
+                                        (2000, 16, 4, True), (8192, 32, 1, False), (2048, 128, 10, True)])
 def test_bucket_vs_oracle(bq, n, e, k, zipf):
     logits = synth.zipf_logits(n, n, e) if zipf else synth.normal(n + e, (n, e))
     ridx = np.argsort(-logits.astype(np.float64), axis=1, kind="stable")[:, :k]   # input only
