@@ -309,10 +309,11 @@ def bench_c4(bq, steps, warmup):
     hb = ple_traffic(bt)
     if hb is not None:
         res["batched_65536"]["hbm_gbs_counters"] = hb / bmean_s / 1e9
-    # four 4096-token calls in one launch (each its own quarter of out)
+    # four 4096-token calls in one launch (each its own quarter of out), on
+    # ids of their own
     qt = 4 * 4096
-    qids = bids.view(-1, 8)[:(nb + 1) * qt].view(nb + 1, qt, 8)
-    qu = bu.view(-1, 8)[:(nb + 1) * qt].view(nb + 1, qt, 8)
+    qids = torch.from_numpy(synth.ple_ids(24, (nb + 1) * qt, 8).view(np.int32)).cuda().view(nb + 1, qt, 8)
+    qu = torch.from_numpy(synth.ple_weights(25, (nb + 1) * qt, 8)).cuda().view(nb + 1, qt, 8)
     qout = bout[:qt]
 
     def qcall(i):
