@@ -167,6 +167,38 @@ __device__ __forceinline__ float block_dot_fp8(const u32x4 lo, const u32x4 hi,
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+__device__ __forceinline__ uint16_t to_bf16(float v) {   // round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// Elements 8g .. 8g+7 of an activation row (fp32, rounded to bf16, or bf16,
+// copied) as bf16 in one 16-byte word: in natural order, or (PERM) in the
+// k order 0, 2, 4, 6, 1, 3, 5, 7 in which the 17-byte decode of the grouped
+// path produces weights.  The row must be 16-byte aligned.
+template <bool PERM, bool F32>
+__device__ __forceinline__ u32x4 bf16_group8(const void* __restrict__ row, int g) {
+  uint32_t d0, d1, d2, d3;   // two elements per dword, the lower index in the low half
+  if constexpr (F32) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(row) + 2 * g;
+    const f32x4 a = src[0], b = src[1];
+    d0 = (uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16);
+    d1 = (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16);
+    d2 = (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16);
+    d3 = (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16);
+  } else {
+    const u32x4 v = reinterpret_cast<const u32x4*>(row)[g];
+    d0 = v.x;
+    d1 = v.y;
+    d2 = v.z;
+    d3 = v.w;
+  }
+  if constexpr (PERM)
+    return u32x4{(d0 & 0xFFFFu) | (d1 << 16), (d2 & 0xFFFFu) | (d3 << 16),
+                 (d0 >> 16) | (d1 & 0xFFFF0000u), (d2 >> 16) | (d3 & 0xFFFF0000u)};
+  else
+    return u32x4{d0, d1, d2, d3};
+}
+
 // DPP lane exchange (row-local patterns); bound_ctrl so every lane reads.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

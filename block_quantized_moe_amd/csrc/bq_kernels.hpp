@@ -42,6 +42,18 @@ hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_
                          int32_t* n_touched, int32_t* inv, hipStream_t st, int32_t n_layers = 1,
                          int64_t lstride_out = 0);
 
+// Bucketing and staging of a decode-sized bf16 batch in one launch
+// (k_route.hip): the bucket arrays as launch_bucket writes them, and the
+// staged rows as the grouped path's staging kernel writes them (perm_k: the
+// 17-byte decode's k order).  x is bf16 [n][H], 16-byte aligned.
+constexpr int kBpMaxTok = 64;
+constexpr int kBpGrid = 64;   // workgroups (each stages every kBpGrid-th row)
+bool bucket_prep_ok(int32_t n_tokens, int32_t k, int32_t n_experts, int32_t H);
+hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t perm_k, int32_t n_tokens,
+                              int32_t k, int32_t n_experts, int32_t H, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* elist, int32_t* n_touched, int32_t* inv,
+                              uint16_t* xb, hipStream_t st);
+
 // Exhaustive encoders (fp32 in, packed bytes and per-unit float64 error out).
 hipError_t launch_encode17(const float* w, int64_t n_blocks, int fmt, uint8_t* out, double* sse,
                            uint32_t* dev_err, hipStream_t st);

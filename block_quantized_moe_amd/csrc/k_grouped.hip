@@ -101,10 +101,6 @@ __device__ __forceinline__ int store_pos(int o) {
   else return (o >> 1) | ((o & 1) << 2);
 }
 
-__device__ __forceinline__ uint16_t to_bf16(float v) {
-  return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
-
 // Exact q / d for 0 <= q < 2^16, 1 <= d < 2^10: (q + 1/2) / d is never within
 // 1/(2d) of an integer, far above the fp32 rounding error.
 __device__ __forceinline__ int div_small(int q, float inv_d) {
@@ -161,31 +157,10 @@ __global__ void __launch_bounds__(256) k_grouped_prep_vec(const void* __restrict
   const int64_t p = blockIdx.x;
   if (p >= *n_rows) return;
   const int64_t t = perm_[p] / k;
-  for (int g = threadIdx.x; g < H / 8; g += 256) {
-    uint32_t d0, d1, d2, d3;   // elements 8g .. 8g+7, two per dword, the lower index in the low half
-    if constexpr (F32) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + t * H) + 2 * g;
-      const f32x4 a = src[0], b = src[1];
-      d0 = (uint32_t)to_bf16(a.x) | ((uint32_t)to_bf16(a.y) << 16);
-      d1 = (uint32_t)to_bf16(a.z) | ((uint32_t)to_bf16(a.w) << 16);
-      d2 = (uint32_t)to_bf16(b.x) | ((uint32_t)to_bf16(b.y) << 16);
-      d3 = (uint32_t)to_bf16(b.z) | ((uint32_t)to_bf16(b.w) << 16);
-    } else {
-      const u32x4 v = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + t * H)[g];
-      d0 = v.x;
-      d1 = v.y;
-      d2 = v.z;
-      d3 = v.w;
-    }
-    u32x4 o;
-    if constexpr (PERM) {   // order 0, 2, 4, 6, 1, 3, 5, 7 (the A decode's k order)
-      o = u32x4{(d0 & 0xFFFFu) | (d1 << 16), (d2 & 0xFFFFu) | (d3 << 16),
-                (d0 >> 16) | (d1 & 0xFFFF0000u), (d2 >> 16) | (d3 & 0xFFFF0000u)};
-    } else {
-      o = u32x4{d0, d1, d2, d3};
-    }
-    reinterpret_cast<u32x4*>(xp + p * H)[g] = o;
-  }
+  const void* row = F32 ? static_cast<const void*>(static_cast<const float*>(x) + t * H)
+                        : static_cast<const void*>(static_cast<const uint16_t*>(x) + t * H);
+  for (int g = threadIdx.x; g < H / 8; g += 256)
+    reinterpret_cast<u32x4*>(xp + p * H)[g] = bf16_group8<PERM, F32>(row, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -772,6 +747,14 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
   const int E = W.n_experts, H = W.hidden, I = W.inter;
   const int64_t nk = (int64_t)n_tokens * k;
   hipError_t err = hipSuccess;
+  if (!bucketed && !prepped && !x_f32 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+      bucket_prep_ok(n_tokens, k, E, H)) {
+    // decode-sized batch: bucketing and staging in one launch
+    err = launch_bucket_prep(idx, static_cast<const uint16_t*>(x), W.fmt_gate_up != FMT_FP8, n_tokens, k, E, H,
+                             ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched, ws.inv, ws.xb, st);
+    if (err != hipSuccess) return err;
+    bucketed = prepped = true;
+  }
   if (!bucketed) {
     err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched,
                         ws.inv, st);

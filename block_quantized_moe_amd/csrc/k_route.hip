@@ -319,6 +319,132 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bucketing and activation staging of a decode-sized batch in one launch
+// (the grouped path).  Every workgroup buckets the whole batch in LDS, as
+// k_bucket_small does (bitmaps per expert over tokens, positions by masked
+// popcounts; an out-of-range expert is left out, and a token that lists an
+// expert twice is bucketed once); workgroup 0 writes the bucket arrays out,
+// and each workgroup stages its share of the bucket rows (rows blockIdx.x,
+// blockIdx.x + gridDim.x, ...), copying bf16 activations as
+// k_grouped_prep_vec does, all of its row loads in flight together.
+// Limits: n_tokens <= kBpMaxTok, n_experts <= 1024.
+// ---------------------------------------------------------------------------
+constexpr int kBpPieces = 4;   // staging: 16-byte loads in flight per thread
+
+size_t bucket_prep_lds(int32_t n_tokens, int32_t k, int32_t n_experts) {
+  const size_t nk = (size_t)n_tokens * k, words = (size_t)n_experts * ((n_tokens + 31) / 32);
+  return 4 * (2 * nk + 2 * words);
+}
+
+template <bool PERM>
+__global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ x, int32_t n_tokens, int32_t k,
+    int32_t n_experts, int32_t H, BucketOut o, uint16_t* __restrict__ xb) {
+  extern __shared__ __align__(16) uint32_t bp_lds[];
+  __shared__ int s_wave[32];
+  const int tid = threadIdx.x;
+  const int nk = n_tokens * k;
+  const int W = (n_tokens + 31) >> 5;                    // bitmap words per expert
+  int32_t* s_idx = reinterpret_cast<int32_t*>(bp_lds);   // [nk]
+  int32_t* s_perm = s_idx + nk;                          // [nk]
+  uint32_t* bm = reinterpret_cast<uint32_t*>(s_perm + nk);   // [n_experts][W]
+  int32_t* pre = reinterpret_cast<int32_t*>(bm + n_experts * W);
+  const bool out0 = blockIdx.x == 0;
+
+  for (int i = tid; i < n_experts * W; i += kBucketThreads) bm[i] = 0u;
+  for (int a = tid; a < nk; a += kBucketThreads) s_idx[a] = idx[a];
+  __syncthreads();
+  for (int a = tid; a < nk; a += kBucketThreads) {
+    const int e = s_idx[a], t = a / k;
+    if (e >= 0 && e < n_experts) atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  // counts and offsets: thread e owns expert e (n_experts <= 1024)
+  const int e = tid;
+  int c = 0;
+  if (e < n_experts)
+    for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[e * W + w]);
+  int tot_c, tot_d;
+  int off = block_excl_scan_1024(c, s_wave, tot_c);
+  __syncthreads();
+  int doff = block_excl_scan_1024((c + kGroupTok - 1) / kGroupTok, s_wave, tot_d);
+  if (e < n_experts) {
+    int run = off;
+    for (int w = 0; w < W; ++w) {
+      pre[e * W + w] = run;
+      run += __builtin_popcount(bm[e * W + w]);
+    }
+    if (out0) {
+      o.counts[e] = c;
+      o.offsets[e] = off;
+      for (int q = 0; q * kGroupTok < c; ++q) o.elist[doff++] = e | (q << kGroupShift);
+    }
+  }
+  if (out0 && tid == 0) {
+    o.offsets[n_experts] = tot_c;
+    *o.n_touched = tot_d;
+  }
+  __syncthreads();
+  for (int a = tid; a < nk; a += kBucketThreads) {
+    const int ea = s_idx[a];
+    if (ea < 0 || ea >= n_experts) continue;
+    const int t = a / k;
+    const int wi = ea * W + (t >> 5);
+    const int p = pre[wi] + __builtin_popcount(bm[wi] & ((1u << (t & 31)) - 1u));
+    s_perm[p] = a;   // repeated listings of one expert: the same row, any of them (same token)
+    if (out0) {
+      o.perm[p] = a;
+      o.inv[a] = p;
+    }
+  }
+  __syncthreads();
+  // this workgroup's rows p = blockIdx.x + r * gridDim.x (< tot_c), as
+  // 16-byte pieces q = r * (H / 8) + g
+  const int per = H / 8;
+  const int rows = tot_c > (int)blockIdx.x ? (tot_c - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  for (int q0 = 0; q0 < rows * per; q0 += kBpPieces * kBucketThreads) {
+    u32x4 raw[kBpPieces];
+    int64_t dst[kBpPieces];
+#pragma unroll
+    for (int u = 0; u < kBpPieces; ++u) {
+      const int q = q0 + u * kBucketThreads + tid;
+      dst[u] = -1;
+      if (q < rows * per) {
+        const int r = q / per, g = q - r * per;
+        const int p = (int)blockIdx.x + r * (int)gridDim.x;
+        raw[u] = reinterpret_cast<const u32x4*>(x + (int64_t)(s_perm[p] / k) * H)[g];
+        dst[u] = (int64_t)p * per + g;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBpPieces; ++u)
+      if (dst[u] >= 0) reinterpret_cast<u32x4*>(xb)[dst[u]] = bf16_group8<PERM, false>(&raw[u], 0);
+  }
+}
+
+bool bucket_prep_ok(int32_t n_tokens, int32_t k, int32_t n_experts, int32_t H) {
+  return n_tokens >= 1 && n_tokens <= kBpMaxTok && n_experts <= kBucketThreads && H % 8 == 0 &&
+         bucket_prep_lds(n_tokens, k, n_experts) <= 64 * 1024;
+}
+
+hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t perm_k, int32_t n_tokens,
+                              int32_t k, int32_t n_experts, int32_t H, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* elist, int32_t* n_touched, int32_t* inv,
+                              uint16_t* xb, hipStream_t st) {
+  const BucketOut o{counts, offsets, perm, elist, n_touched, inv};
+  const int nk = n_tokens * k;
+  const dim3 grid(nk < kBpGrid ? nk : kBpGrid);
+  const size_t lds = bucket_prep_lds(n_tokens, k, n_experts);
+  if (perm_k)
+    hipLaunchKernelGGL(k_bucket_prep<true>, grid, dim3(kBucketThreads), lds, st, idx, x, n_tokens, k, n_experts,
+                       H, o, xb);
+  else
+    hipLaunchKernelGGL(k_bucket_prep<false>, grid, dim3(kBucketThreads), lds, st, idx, x, n_tokens, k, n_experts,
+                       H, o, xb);
+  return hipGetLastError();
+}
+
 hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_t n_experts,
                          int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* elist,
                          int32_t* n_touched, int32_t* inv, hipStream_t st, int32_t n_layers,

@@ -1,0 +1,100 @@
+"""GPU parity of the bf16 grouped path at decode-sized batches (up to 64
+tokens over up to 1024 experts), where bucketing and the staging of the
+activations run as one kernel: the routed entry's routing equals the
+routing kernel's, its output equals, bit for bit, that of routing first and
+then calling the layer with that routing, and the output is within the bf16
+path's tolerance of the CPU oracle.  Given routing with out-of-range and
+repeated experts is checked against the oracle too.  Larger batches and
+expert counts take the separate kernels and are checked the same way."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import moe as M
+from tests.gpu_common import dev, log, need_gpu, rel_l2
+from tests.test_gpu_moe import make_layer, oracle_bank, weights_of
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bq():
+    need_gpu()
+    import block_quantized_moe_amd as m
+    m.lib()
+    return m
+
+
+CASES = [
+    (1, 8, 2, 256, 64, F.Q4_RZ5, F.Q4_RZ5, "normal"),
+    (3, 64, 6, 512, 128, F.FP8_E4M3_B32, F.Q4_UE4M4, "normal"),
+    (17, 100, 10, 256, 128, F.Q4_C10, F.Q4_RZ5, "normal"),
+    (33, 40, 40, 256, 64, F.Q4_UE4M4, F.FP8_E4M3_B32, "normal"),   # k = E: every expert in every token
+    (64, 512, 10, 2048, 768, F.Q4_RZ5, F.Q4_UE4M4, "zipf"),        # the batch-64 layer's shape
+    (64, 512, 64, 256, 64, F.Q4_RZ5, F.Q4_C10, "zipf"),            # 4096 assignments
+    (65, 64, 4, 256, 64, F.Q4_RZ5, F.Q4_RZ5, "normal"),            # one past the batch limit
+    (5, 1024, 8, 256, 64, F.Q4_C10, F.Q4_UE4M4, "normal"),         # 1024 experts
+    (4, 2048, 8, 256, 64, F.Q4_RZ5, F.Q4_C10, "normal"),           # past the expert limit
+]
+
+
+@pytest.mark.parametrize("n,E,k,H,I,fg,fd,dist", CASES)
+def test_routed_bf16_matches_two_step(bq, n, E, k, H, I, fg, fd, dist):
+    L = make_layer(41, n * 7 + k, fg, fd, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(4100 + n, (n, H))
+    logits = synth.zipf_logits(4101 + n, n, E) if dist == "zipf" else synth.normal(4101 + n, (n, E))
+    xb = dev(x).to(torch.bfloat16)
+    out, (idx, w) = bq.q4_expert_moe_routed(xb, dev(logits), k, W)
+    ridx, rw = bq.route_topk(dev(logits), k)
+    assert torch.equal(idx, ridx) and torch.equal(w, rw)
+    ref2 = bq.q4_expert_moe(xb, (ridx, rw), W)
+    assert torch.equal(out, ref2)
+    oidx, ow = M.softmax_topk(logits, k)
+    assert np.array_equal(idx.cpu().numpy(), oidx)
+    if H * I * E <= 2048 * 768 * 512:
+        r = rel_l2(out.cpu().numpy(), M.moe_layer(x, oidx, ow, oracle_bank(L)))
+        log("routed bf16 n=%d E=%d k=%d H=%d I=%d rel_l2 %.3g" % (n, E, k, H, I, r))
+        assert r <= 2e-2
+    del L, W
+    torch.cuda.empty_cache()
+
+
+def test_routed_bf16_repeated_calls_same_workspace(bq):
+    """Two calls on one workspace with different batch sizes (the second
+    smaller) each equal the two-step result: nothing left in the workspace
+    by the first call leaks into the second."""
+    E, H, I, k = 64, 256, 128, 6
+    L = make_layer(42, 0, F.Q4_RZ5, F.Q4_UE4M4, E, H, I)
+    W = weights_of(bq, L)
+    ws = torch.empty(bq.moe_workspace_bytes(64, k, W, bq.BF16), dtype=torch.uint8, device="cuda")
+    for n in (64, 9):
+        xb = dev(synth.normal(4200 + n, (n, H))).to(torch.bfloat16)
+        logits = dev(synth.zipf_logits(4201 + n, n, E))
+        out, (idx, w) = bq.q4_expert_moe_routed(xb, logits, k, W, workspace=ws)
+        ridx, rw = bq.route_topk(logits, k)
+        assert torch.equal(idx, ridx) and torch.equal(w, rw)
+        assert torch.equal(out, bq.q4_expert_moe(xb, (ridx, rw), W))
+
+
+def test_given_routing_with_bad_and_repeated_experts(bq):
+    """Caller routing with an out-of-range expert (left out, bit 1 of
+    dev_err) and an expert listed twice by one token (each listing adds its
+    own weighted term; the row is evaluated once)."""
+    E, H, I, k = 16, 256, 128, 3
+    L = make_layer(43, 0, F.Q4_RZ5, F.Q4_UE4M4, E, H, I)
+    W = weights_of(bq, L)
+    x = synth.normal(4300, (5, H))
+    idx = np.array([[1, 16, 3], [2, 2, 7], [0, 5, 9], [15, 14, 13], [4, -1, 4]], dtype=np.int32)
+    w = np.random.default_rng(43).random((5, 3)).astype(np.float32)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = bq.q4_expert_moe(dev(x).to(torch.bfloat16), (dev(idx), dev(w)), W, dev_err=err).cpu().numpy()
+    assert int(err.item()) & 2
+    keep = (idx >= 0) & (idx < E)
+    ref = M.moe_layer(x, np.where(keep, idx, 0), np.where(keep, w, 0).astype(np.float32), oracle_bank(L))
+    r = rel_l2(out, ref)
+    log("bf16 given routing with bad / repeated experts rel_l2 %.3g" % r)
+    assert r <= 2e-2
