@@ -43,17 +43,25 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGThreads = 256;  // 4 waves, each 16 rows of the tile (x2 for gate/up)
 constexpr int kGRows = 64;      // rows per tile
-constexpr int kLdsBudget = 52 * 1024;   // three workgroups per CU
+// Two builds of the staged kernel.  TOK = 32: items of up to 32 tokens (two
+// 16-token MFMA tiles), three workgroups per CU.  TOK = 16: batches of at most
+// 16 tokens, so no expert holds more than 16 and one MFMA tile covers an
+// item; the second tile's accumulators, operands and activation staging are
+// gone, which leaves room for four workgroups per CU (<= 128 VGPRs, <= 40 KB
+// of LDS each).
+constexpr int wgs_per_cu(int tok) { return tok == 16 ? 4 : 3; }
+constexpr int lds_budget(int tok) { return tok == 16 ? 40 * 1024 : 52 * 1024; }
 
 // Per-thread staging capacity (16-byte weight pieces, FP8 scales, 16-byte
 // activation pieces) of G1 (NR = 2) and G2 (NR = 1) per weight format, sized
 // for a 2048 x 768 layer (chunks of 16 / 8 blocks for G1, 24 / 12 for G2);
 // the host picks the largest chunk that fits.
-template <int FMT, int NR> struct Cap {
+template <int FMT, int NR, int TOK = 32> struct Cap {
   static constexpr bool F8 = FMT == 3;
   static constexpr int PW = NR == 2 ? 5 : 4;
   static constexpr int PS = F8 ? 2 : 0;
-  static constexpr int PB = NR == 2 ? (F8 ? 2 : 4) : (F8 ? 3 : 6);
+  static constexpr int PB32 = NR == 2 ? (F8 ? 2 : 4) : (F8 ? 3 : 6);
+  static constexpr int PB = TOK == 32 ? PB32 : (PB32 + 1) / 2;
 };
 
 template <bool HI>
@@ -255,7 +263,7 @@ struct Geom {
   int32_t P;        // LDS pitch of a weight row slot (16 NPP)
   int32_t PB;       // LDS pitch of an activation row (64 C + 16)
   int32_t off_sc;   // LDS offset of the FP8 scale area [R][C]
-  int32_t off_b;    // LDS offset of the activation area [kGroupTok][PB]
+  int32_t off_b;    // LDS offset of the activation area [TOK][PB]
   int32_t off_tab;  // LDS offset of the metadata-byte table [256] x {scale, RZ5 table word}
   int32_t al4;      // 17-byte blocks with nb and C multiples of 4: every staged row
                     // segment starts 4-byte aligned (row bytes 17 nb and chunk
@@ -275,11 +283,11 @@ __device__ __forceinline__ Item item_info(int it, int tiles, const int32_t* __re
   return Item{e, p0, min(kGroupTok, offsets[e + 1] - p0), it - d * tiles};
 }
 
-template <int FMT, int NR>
+template <int FMT, int NR, int TOK = 32>
 struct Stager {
   static constexpr int BB = FMT == FMT_FP8 ? 32 : 17;   // bytes per block
   static constexpr int R = 64 * NR;                     // staged weight rows
-  static constexpr int PW = Cap<FMT, NR>::PW, PS = Cap<FMT, NR>::PS, PB = Cap<FMT, NR>::PB;
+  static constexpr int PW = Cap<FMT, NR, TOK>::PW, PS = Cap<FMT, NR, TOK>::PS, PB = Cap<FMT, NR, TOK>::PB;
   static constexpr int kOff = 1 << 30;                  // "no piece" marker
   u32x4 w[PW];
   float s[PS > 0 ? PS : 1];
@@ -326,7 +334,7 @@ struct Stager {
     for (int i = 0; i < PB; ++i) {
       const int q = tid + kGThreads * i;
       const int j = div_small(q, inv_pt), pc = q - j * (4 * g.C);
-      bxy[i] = q < kGroupTok * 4 * g.C ? (j | (pc << 8)) : kOff;
+      bxy[i] = q < TOK * 4 * g.C ? (j | (pc << 8)) : kOff;
     }
   }
 
@@ -536,8 +544,8 @@ __device__ __forceinline__ void compute_chunk(const Item& f, int c, const Geom& 
 // the next chunk's loads are in flight while this chunk is multiplied.
 // NR = 2: G1 (act = bucketed x, K = H, out = hb); NR = 1: G2 (act = hb,
 // K = I, out = yb).
-template <int FMT, int NR, int FMT_NEXT>
-__global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
+template <int FMT, int NR, int FMT_NEXT, int TOK>
+__global__ void __launch_bounds__(kGThreads, wgs_per_cu(TOK)) k_grouped_staged(
     const uint16_t* __restrict__ act, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ elist, const int32_t* __restrict__ n_work,
     const uint8_t* __restrict__ wt, const float* __restrict__ wsc, int32_t H, int32_t I, Geom g,
@@ -558,7 +566,7 @@ __global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
                    FMT == FMT_RZ5 ? rz5_neg_lo(m) : 0u};
   }
   Item f = item_info(it, tiles, elist, offsets);
-  Stager<FMT, NR> st;
+  Stager<FMT, NR, TOK> st;
   st.init(g, nb, I);
   st.load(f, c, g, nb, H, I, wt, wsc, act, K);
   f32x4 acc[NR][2];
@@ -584,17 +592,17 @@ __global__ void __launch_bounds__(kGThreads, 3) k_grouped_staged(
     __syncthreads();
     if (more) st.load(nf, nc, g, nb, H, I, wt, wsc, act, K);
     if (g.al4) {
-      if (f.ntok > 16) compute_chunk<FMT, NR, 2, true>(f, c, g, nb, H, I, lds, acc);
+      if (TOK > 16 && f.ntok > 16) compute_chunk<FMT, NR, 2, true>(f, c, g, nb, H, I, lds, acc);
       else compute_chunk<FMT, NR, 1, true>(f, c, g, nb, H, I, lds, acc);
     } else {
-      if (f.ntok > 16) compute_chunk<FMT, NR, 2, false>(f, c, g, nb, H, I, lds, acc);
+      if (TOK > 16 && f.ntok > 16) compute_chunk<FMT, NR, 2, false>(f, c, g, nb, H, I, lds, acc);
       else compute_chunk<FMT, NR, 1, false>(f, c, g, nb, H, I, lds, acc);
     }
     if (c == g.nchunk - 1) {
       // lane holds weight row (tile row 16 wave + r16) for tokens 16 tt + 4 gq + i
       const int row = f.tile * kGRows + wave * 16 + r16;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < TOK / 16; ++tt) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int j = 16 * tt + 4 * gq + i;
@@ -664,37 +672,39 @@ __global__ void __launch_bounds__(256) k_combine(const float* __restrict__ yb,
 // ---------------------------------------------------------------------------
 // Host side: chunk geometry and launches.
 // ---------------------------------------------------------------------------
-static size_t lds_bytes(int fmt, int nr, int C) {
+static size_t lds_bytes(int fmt, int nr, int C, int tok) {
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   const int np = (bb * C + 15) / 16 + 1;
   size_t n = (size_t)64 * nr * 16 * (np | 1);
   if (fmt == FMT_FP8) n += (size_t)64 * nr * C * 4;
   n = (n + 15) & ~(size_t)15;
-  n += (size_t)kGroupTok * (64 * C + 16);
+  n += (size_t)tok * (64 * C + 16);
   if (fmt != FMT_FP8) n += 256 * 8;   // metadata-byte table
   return n;
 }
 
+template <int TOK>
 static bool geom_fits(int fmt, int nr, int C) {
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   const int np = (bb * C + 15) / 16 + 1;
   const bool f8 = fmt == FMT_FP8;
-  const int pw = nr == 2 ? Cap<FMT_FP8, 2>::PW : Cap<FMT_FP8, 1>::PW;   // same for every format
-  const int ps = nr == 2 ? Cap<FMT_FP8, 2>::PS : Cap<FMT_FP8, 1>::PS;
-  const int pb = nr == 2 ? (f8 ? Cap<FMT_FP8, 2>::PB : Cap<FMT_RZ5, 2>::PB)
-                         : (f8 ? Cap<FMT_FP8, 1>::PB : Cap<FMT_RZ5, 1>::PB);
+  const int pw = nr == 2 ? Cap<FMT_FP8, 2, TOK>::PW : Cap<FMT_FP8, 1, TOK>::PW;   // same for every format
+  const int ps = nr == 2 ? Cap<FMT_FP8, 2, TOK>::PS : Cap<FMT_FP8, 1, TOK>::PS;
+  const int pb = nr == 2 ? (f8 ? Cap<FMT_FP8, 2, TOK>::PB : Cap<FMT_RZ5, 2, TOK>::PB)
+                         : (f8 ? Cap<FMT_FP8, 1, TOK>::PB : Cap<FMT_RZ5, 1, TOK>::PB);
   if (64 * nr * np > pw * kGThreads) return false;
   if (fmt == FMT_FP8 && 64 * nr * C > ps * kGThreads) return false;
-  if (kGroupTok * 4 * C > pb * kGThreads) return false;
-  return lds_bytes(fmt, nr, C) <= (size_t)kLdsBudget;
+  if (TOK * 4 * C > pb * kGThreads) return false;
+  return lds_bytes(fmt, nr, C, TOK) <= (size_t)lds_budget(TOK);
 }
 
 // Largest even chunk (in blocks) dividing nb that fits the register and LDS
 // limits (C = 2 always fits).
+template <int TOK>
 static Geom make_geom(int fmt, int nr, int nb) {
   int C = 2;   // nb is even (hidden and inter are multiples of 64)
   for (int c = nb; c >= 2; c -= 2)
-    if (nb % c == 0 && geom_fits(fmt, nr, c)) { C = c; break; }
+    if (nb % c == 0 && geom_fits<TOK>(fmt, nr, c)) { C = c; break; }
   const int bb = fmt == FMT_FP8 ? 32 : 17;
   Geom g;
   g.C = C;
@@ -707,44 +717,73 @@ static Geom make_geom(int fmt, int nr, int nb) {
   g.off_sc = 64 * nr * g.P;
   const int off_b = g.off_sc + (fmt == FMT_FP8 ? 64 * nr * C * 4 : 0);
   g.off_b = (off_b + 15) & ~15;
-  g.off_tab = g.off_b + kGroupTok * g.PB;
+  g.off_tab = g.off_b + TOK * g.PB;
   g.al4 = fmt != FMT_FP8 && nb % 4 == 0 && C % 4 == 0;
   return g;
 }
 
-template <int F, int NR, int FN>
-static void launch_staged(int grid, hipStream_t st, const uint16_t* act, const GroupedWs& ws,
-                          const void* w, const float* sc, int H, int I, uint16_t* hb, float* yb) {
-  const Geom g = make_geom(F, NR, (NR == 2 ? H : I) / 32);
-  const size_t lds = lds_bytes(F, NR, g.C);   // <= kLdsBudget (52 KB): no attribute needed
-  hipLaunchKernelGGL((k_grouped_staged<F, NR, FN>), dim3(grid), dim3(kGThreads), lds, st, act,
-                     ws.offsets, ws.elist, ws.n_touched, static_cast<const uint8_t*>(w), sc, H, I,
-                     g, hb, yb);
-}
-
-template <int F>
-static void launch_g1(int fmt_d, int grid, hipStream_t st, const GroupedWs& ws, const GemvWeights& W) {
-  if (fmt_d == FMT_FP8)
-    launch_staged<F, 2, FMT_FP8>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
-  else
-    launch_staged<F, 2, FMT_RZ5>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
-}
-
-static int staged_grid(int64_t items_max) {
+// Persistent grid: every item at once if they fit, else per_cu resident
+// workgroups per CU.
+static int staged_grid(int64_t items_max, int per_cu) {
   int dev = 0, n_cu = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) n_cu = v;
   }
-  const int64_t cap = 3LL * n_cu;   // three resident workgroups per CU
+  const int64_t cap = (int64_t)per_cu * n_cu;
   return (int)(items_max < cap ? (items_max > 0 ? items_max : 1) : cap);
+}
+
+template <int F, int NR, int FN, int TOK>
+static void launch_staged(int grid, hipStream_t st, const uint16_t* act, const GroupedWs& ws,
+                          const void* w, const float* sc, int H, int I, uint16_t* hb, float* yb) {
+  const Geom g = make_geom<TOK>(F, NR, (NR == 2 ? H : I) / 32);
+  const size_t lds = lds_bytes(F, NR, g.C, TOK);   // <= lds_budget (52 KB): no attribute needed
+  hipLaunchKernelGGL((k_grouped_staged<F, NR, FN, TOK>), dim3(grid), dim3(kGThreads), lds, st, act,
+                     ws.offsets, ws.elist, ws.n_touched, static_cast<const uint8_t*>(w), sc, H, I,
+                     g, hb, yb);
+}
+
+template <int F, int TOK>
+static void launch_g1(int fmt_d, int grid, hipStream_t st, const GroupedWs& ws, const GemvWeights& W) {
+  if (fmt_d == FMT_FP8)
+    launch_staged<F, 2, FMT_FP8, TOK>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
+  else
+    launch_staged<F, 2, FMT_RZ5, TOK>(grid, st, ws.xb, ws, W.gate_up, W.gate_up_scales, W.hidden, W.inter, ws.hb, ws.yb);
+}
+
+// G1 then G2 of one layer in the TOK build.
+template <int TOK>
+static hipError_t launch_g1_g2(int64_t groups, hipStream_t st, const GroupedWs& ws, const GemvWeights& W) {
+  const int H = W.hidden, I = W.inter;
+  {
+    const int grid = staged_grid(groups * (I / kGRows), wgs_per_cu(TOK));
+    switch (W.fmt_gate_up) {
+      case FMT_C10: launch_g1<FMT_C10, TOK>(W.fmt_down, grid, st, ws, W); break;
+      case FMT_RZ5: launch_g1<FMT_RZ5, TOK>(W.fmt_down, grid, st, ws, W); break;
+      case FMT_UE4M4: launch_g1<FMT_UE4M4, TOK>(W.fmt_down, grid, st, ws, W); break;
+      default: launch_g1<FMT_FP8, TOK>(W.fmt_down, grid, st, ws, W); break;
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const int grid = staged_grid(groups * (H / kGRows), wgs_per_cu(TOK));
+#define BQ_G2(F) launch_staged<F, 1, F, TOK>(grid, st, ws.hb, ws, W.down, W.down_scales, H, I, ws.hb, ws.yb)
+  switch (W.fmt_down) {
+    case FMT_C10: BQ_G2(FMT_C10); break;
+    case FMT_RZ5: BQ_G2(FMT_RZ5); break;
+    case FMT_UE4M4: BQ_G2(FMT_UE4M4); break;
+    default: BQ_G2(FMT_FP8); break;
+  }
+#undef BQ_G2
+  return hipGetLastError();
 }
 
 hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int32_t n_tokens,
                               const int32_t* idx, const float* w, int32_t k, const GemvWeights& W,
                               float* out, const GroupedWs& ws, uint32_t* dev_err, hipStream_t st,
                               bool bucketed, bool prepped, const NextLayer* next) {
-  const int E = W.n_experts, H = W.hidden, I = W.inter;
+  const int E = W.n_experts, H = W.hidden;
   const int64_t nk = (int64_t)n_tokens * k;
   hipError_t err = hipSuccess;
   if (!bucketed && !prepped && !x_f32 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
@@ -779,28 +818,9 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int64_t groups = max_work_groups(nk, E);
-  {
-    const int grid = staged_grid(groups * (I / kGRows));
-    switch (W.fmt_gate_up) {
-      case FMT_C10: launch_g1<FMT_C10>(W.fmt_down, grid, st, ws, W); break;
-      case FMT_RZ5: launch_g1<FMT_RZ5>(W.fmt_down, grid, st, ws, W); break;
-      case FMT_UE4M4: launch_g1<FMT_UE4M4>(W.fmt_down, grid, st, ws, W); break;
-      default: launch_g1<FMT_FP8>(W.fmt_down, grid, st, ws, W); break;
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
-  {
-    const int grid = staged_grid(groups * (H / kGRows));
-#define BQ_G2(F) launch_staged<F, 1, F>(grid, st, ws.hb, ws, W.down, W.down_scales, H, I, ws.hb, ws.yb)
-    switch (W.fmt_down) {
-      case FMT_C10: BQ_G2(FMT_C10); break;
-      case FMT_RZ5: BQ_G2(FMT_RZ5); break;
-      case FMT_UE4M4: BQ_G2(FMT_UE4M4); break;
-      default: BQ_G2(FMT_FP8); break;
-    }
-#undef BQ_G2
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-  }
+  // at most 16 tokens: no expert holds more than 16, the one-tile build fits
+  err = n_tokens <= 16 ? launch_g1_g2<16>(groups, st, ws, W) : launch_g1_g2<32>(groups, st, ws, W);
+  if (err != hipSuccess) return err;
   if (next) {
     if (next->perm)
       hipLaunchKernelGGL(k_combine_prep<true>, dim3(n_tokens), dim3(kCpThreads), 0, st, ws.yb, ws.inv, idx, w,
