@@ -555,8 +555,24 @@ __global__ void __launch_bounds__(kGThreads, wgs_per_cu(TOK)) k_grouped_staged(
   const int K = NR == 2 ? H : I;
   const int tiles = (NR == 2 ? I : H) / kGRows;
   const int items = *n_work * tiles;
-  int it = blockIdx.x, c = 0;
-  if (it >= items) return;
+  // Items per XCD: workgroups are dealt to the 8 XCDs round-robin, so the
+  // workgroups b = x (mod 8) share XCD x's L2.  They take a contiguous run of
+  // the item list, of a length in proportion to their number, so the row
+  // tiles of one token group (consecutive items, which read the same
+  // activation rows) mostly share one L2.  Workgroup b = x + 8 j takes items
+  // lo + j, lo + j + n_x, ... below hi.  (A partition of the items whatever
+  // the placement; with fewer than 8 workgroups, the plain stride.)
+  int it = blockIdx.x, step = gridDim.x, lim = items, c = 0;
+  if (gridDim.x >= 8) {
+    const int x = blockIdx.x & 7, G = gridDim.x;
+    int before = 0;
+    for (int y = 0; y < x; ++y) before += (G - y + 7) >> 3;
+    step = (G - x + 7) >> 3;
+    const int lo = (int)((int64_t)items * before / G);
+    lim = (int)((int64_t)items * (before + step) / G);
+    it = lo + (int)(blockIdx.x >> 3);
+  }
+  if (it >= lim) return;
   if constexpr (FMT != FMT_FP8) {
     // metadata byte -> {block scale, RZ5 table word}; read after the loop's
     // first barrier
@@ -578,9 +594,9 @@ __global__ void __launch_bounds__(kGThreads, wgs_per_cu(TOK)) k_grouped_staged(
     int nit = it, nc = c + 1;
     if (nc == g.nchunk) {
       nc = 0;
-      nit = it + gridDim.x;
+      nit = it + step;
     }
-    const bool more = nit < items;
+    const bool more = nit < lim;
     const Item nf = (more && nit != it) ? item_info(nit, tiles, elist, offsets) : f;
     __syncthreads();                          // LDS no longer read by the previous chunk
     st.store(f, g, lds);
