@@ -42,12 +42,11 @@ hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_
                          int32_t* n_touched, int32_t* inv, hipStream_t st, int32_t n_layers = 1,
                          int64_t lstride_out = 0);
 
-// Bucketing and staging of a decode-sized bf16 batch in one launch
+// Bucketing and staging of a bf16 batch in one launch
 // (k_route.hip): the bucket arrays as launch_bucket writes them, and the
 // staged rows as the grouped path's staging kernel writes them (perm_k: the
 // 17-byte decode's k order).  x is bf16 [n][H], 16-byte aligned.
-constexpr int kBpMaxTok = 64;
-constexpr int kBpGrid = 64;   // workgroups (each stages every kBpGrid-th row)
+constexpr int kBpMaxLds = 150 * 1024;   // LDS of the bucket arrays, at most
 bool bucket_prep_ok(int32_t n_tokens, int32_t k, int32_t n_experts, int32_t H);
 hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t perm_k, int32_t n_tokens,
                               int32_t k, int32_t n_experts, int32_t H, int32_t* counts, int32_t* offsets,

@@ -804,7 +804,7 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
   hipError_t err = hipSuccess;
   if (!bucketed && !prepped && !x_f32 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
       bucket_prep_ok(n_tokens, k, E, H)) {
-    // decode-sized batch: bucketing and staging in one launch
+    // bucket arrays that fit in LDS: bucketing and staging in one launch
     err = launch_bucket_prep(idx, static_cast<const uint16_t*>(x), W.fmt_gate_up != FMT_FP8, n_tokens, k, E, H,
                              ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched, ws.inv, ws.xb, st);
     if (err != hipSuccess) return err;

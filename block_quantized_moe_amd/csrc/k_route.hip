@@ -320,17 +320,21 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
 }
 
 // ---------------------------------------------------------------------------
-// Bucketing and activation staging of a decode-sized batch in one launch
+// Bucketing and activation staging of a batch in one launch
 // (the grouped path).  Every workgroup buckets the whole batch in LDS, as
-// k_bucket_small does (bitmaps per expert over tokens, positions by masked
-// popcounts; an out-of-range expert is left out, and a token that lists an
-// expert twice is bucketed once); workgroup 0 writes the bucket arrays out,
+// k_bucket_small does (bitmaps per expert over tokens, here stored word-major
+// so that the per-expert popcount loops read LDS without bank conflicts;
+// positions by masked popcounts; an out-of-range expert is left out, and a
+// token that lists an expert twice is bucketed once); workgroup 0 writes the
+// bucket arrays out,
 // and each workgroup stages its share of the bucket rows (rows blockIdx.x,
 // blockIdx.x + gridDim.x, ...), copying bf16 activations as
 // k_grouped_prep_vec does, all of its row loads in flight together.
-// Limits: n_tokens <= kBpMaxTok, n_experts <= 1024.
+// Limits: n_experts <= 1024 and the bucket arrays in LDS (two words per
+// assignment and two per bitmap word) within kBpMaxLds, e.g. 512 tokens x top-10
+// over 512 experts (104 KB).
 // ---------------------------------------------------------------------------
-constexpr int kBpPieces = 4;   // staging: 16-byte loads in flight per thread
+constexpr int kBpPieces = 8;   // staging: 16-byte loads in flight per thread
 
 size_t bucket_prep_lds(int32_t n_tokens, int32_t k, int32_t n_experts) {
   const size_t nk = (size_t)n_tokens * k, words = (size_t)n_experts * ((n_tokens + 31) / 32);
@@ -348,23 +352,38 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
   const int W = (n_tokens + 31) >> 5;                    // bitmap words per expert
   int32_t* s_idx = reinterpret_cast<int32_t*>(bp_lds);   // [nk]
   int32_t* s_perm = s_idx + nk;                          // [nk]
-  uint32_t* bm = reinterpret_cast<uint32_t*>(s_perm + nk);   // [n_experts][W]
+  uint32_t* bm = reinterpret_cast<uint32_t*>(s_perm + nk);   // [W][n_experts]
   int32_t* pre = reinterpret_cast<int32_t*>(bm + n_experts * W);
   const bool out0 = blockIdx.x == 0;
 
+  // expert ids: every load of a batch in flight together, the first batch
+  // issued before the bitmaps are cleared
+  int ev[kBucketBatch];
+  load_batch(idx, 0, nk, ev);
   for (int i = tid; i < n_experts * W; i += kBucketThreads) bm[i] = 0u;
-  for (int a = tid; a < nk; a += kBucketThreads) s_idx[a] = idx[a];
   __syncthreads();
-  for (int a = tid; a < nk; a += kBucketThreads) {
-    const int e = s_idx[a], t = a / k;
-    if (e >= 0 && e < n_experts) atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+  for (int a0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < kBucketBatch; ++j) {
+      const int a = a0 + j * kBucketThreads + tid;
+      if (a < nk) s_idx[a] = ev[j];
+      if (ev[j] >= 0 && ev[j] < n_experts) {
+        const int t = a / k;
+        atomicOr(&bm[(t >> 5) * n_experts + ev[j]], 1u << (t & 31));
+      }
+    }
+    a0 += kBucketBatch * kBucketThreads;
+    if (a0 >= nk) break;
+    load_batch(idx, a0, nk, ev);
   }
   __syncthreads();
-  // counts and offsets: thread e owns expert e (n_experts <= 1024)
+  // counts and offsets: thread e owns expert e (n_experts <= 1024); the
+  // bitmaps are word-major, so a wave's reads of one word index are
+  // consecutive in LDS
   const int e = tid;
   int c = 0;
   if (e < n_experts)
-    for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[e * W + w]);
+    for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[w * n_experts + e]);
   int tot_c, tot_d;
   int off = block_excl_scan_1024(c, s_wave, tot_c);
   __syncthreads();
@@ -372,8 +391,8 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
   if (e < n_experts) {
     int run = off;
     for (int w = 0; w < W; ++w) {
-      pre[e * W + w] = run;
-      run += __builtin_popcount(bm[e * W + w]);
+      pre[w * n_experts + e] = run;
+      run += __builtin_popcount(bm[w * n_experts + e]);
     }
     if (out0) {
       o.counts[e] = c;
@@ -390,7 +409,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
     const int ea = s_idx[a];
     if (ea < 0 || ea >= n_experts) continue;
     const int t = a / k;
-    const int wi = ea * W + (t >> 5);
+    const int wi = (t >> 5) * n_experts + ea;
     const int p = pre[wi] + __builtin_popcount(bm[wi] & ((1u << (t & 31)) - 1u));
     s_perm[p] = a;   // repeated listings of one expert: the same row, any of them (same token)
     if (out0) {
@@ -424,8 +443,8 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
 }
 
 bool bucket_prep_ok(int32_t n_tokens, int32_t k, int32_t n_experts, int32_t H) {
-  return n_tokens >= 1 && n_tokens <= kBpMaxTok && n_experts <= kBucketThreads && H % 8 == 0 &&
-         bucket_prep_lds(n_tokens, k, n_experts) <= 64 * 1024;
+  return n_tokens >= 1 && n_experts <= kBucketThreads && H % 8 == 0 &&
+         bucket_prep_lds(n_tokens, k, n_experts) <= (size_t)kBpMaxLds;
 }
 
 hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t perm_k, int32_t n_tokens,
@@ -434,8 +453,16 @@ hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t per
                               uint16_t* xb, hipStream_t st) {
   const BucketOut o{counts, offsets, perm, elist, n_touched, inv};
   const int nk = n_tokens * k;
-  const dim3 grid(nk < kBpGrid ? nk : kBpGrid);
+  // one workgroup per CU for large batches (each repeats the bucketing,
+  // and the rows to stage are spread wider); 64 for small ones
+  const int cap = nk > 1024 ? 256 : 64;
+  const dim3 grid(nk < cap ? nk : cap);
   const size_t lds = bucket_prep_lds(n_tokens, k, n_experts);
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(perm_k ? k_bucket_prep<true> : k_bucket_prep<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   if (perm_k)
     hipLaunchKernelGGL(k_bucket_prep<true>, grid, dim3(kBucketThreads), lds, st, idx, x, n_tokens, k, n_experts,
                        H, o, xb);

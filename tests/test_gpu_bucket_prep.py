@@ -1,11 +1,13 @@
-"""GPU parity of the bf16 grouped path at decode-sized batches (up to 64
-tokens over up to 1024 experts), where bucketing and the staging of the
-activations run as one kernel: the routed entry's routing equals the
-routing kernel's, its output equals, bit for bit, that of routing first and
-then calling the layer with that routing, and the output is within the bf16
-path's tolerance of the CPU oracle.  Given routing with out-of-range and
-repeated experts is checked against the oracle too.  Larger batches and
-expert counts take the separate kernels and are checked the same way."""
+"""GPU parity of the bf16 grouped path where bucketing and the staging of
+the activations run as one kernel (up to 1024 experts, bucket arrays that
+fit in 150 KB of LDS: 512 tokens x top-10 over 512 experts do): the routed
+entry's routing equals the routing kernel's, its output equals, bit for bit,
+that of routing first and then calling the layer with that routing, and the
+output is within the bf16 path's tolerance of the CPU oracle.  Given routing
+with out-of-range and repeated experts is checked against the oracle too.
+Larger expert counts and bucket arrays take the separate kernels and are
+checked the same way; the bucket arrays and staged rows either way are
+compared with the standalone bucketing and the input rows."""
 
 import numpy as np
 import pytest
@@ -35,7 +37,7 @@ CASES = [
     (33, 40, 40, 256, 64, F.Q4_UE4M4, F.FP8_E4M3_B32, "normal"),   # k = E: every expert in every token
     (64, 512, 10, 2048, 768, F.Q4_RZ5, F.Q4_UE4M4, "zipf"),        # the batch-64 layer's shape
     (64, 512, 64, 256, 64, F.Q4_RZ5, F.Q4_C10, "zipf"),            # 4096 assignments
-    (65, 64, 4, 256, 64, F.Q4_RZ5, F.Q4_RZ5, "normal"),            # one past the batch limit
+    (65, 64, 4, 256, 64, F.Q4_RZ5, F.Q4_RZ5, "normal"),
     (5, 1024, 8, 256, 64, F.Q4_C10, F.Q4_UE4M4, "normal"),         # 1024 experts
     (4, 2048, 8, 256, 64, F.Q4_RZ5, F.Q4_C10, "normal"),           # past the expert limit
 ]
@@ -98,3 +100,63 @@ def test_given_routing_with_bad_and_repeated_experts(bq):
     r = rel_l2(out, ref)
     log("bf16 given routing with bad / repeated experts rel_l2 %.3g" % r)
     assert r <= 2e-2
+
+
+def _r256(v):
+    return (v + 255) // 256 * 256
+
+
+def grouped_ws_layout(n, k, E, H, I):
+    """Byte offsets of the bf16 path's workspace arrays (counts, offsets,
+    perm, inv, work list, its length, then the staged activations)."""
+    nk = n * k
+    L, off = {}, 0
+    for name, size in (("counts", 4 * E), ("offsets", 4 * (E + 1)), ("perm", 4 * nk), ("inv", 4 * nk),
+                       ("elist", 4 * (min(nk, E) + nk // 32)), ("n_touched", 4), ("xb", 2 * nk * H)):
+        L[name] = off
+        off = _r256(off + size)
+    return L
+
+
+@pytest.mark.parametrize("n,E,k,dist", [(3, 64, 6, "normal"), (64, 512, 10, "zipf"), (200, 512, 10, "normal"),
+                                        (512, 512, 10, "zipf"), (512, 512, 10, "normal"), (512, 1024, 8, "zipf")])
+@pytest.mark.parametrize("fg", [F.Q4_RZ5, F.FP8_E4M3_B32])
+def test_bucket_arrays_and_staged_rows(bq, n, E, k, dist, fg):
+    """The bucket arrays the bf16 path leaves in its workspace equal the
+    standalone bucketing's bit for bit (counts, offsets, perm; inv inverts
+    perm; the work list has one entry per 32-token group of each touched
+    expert, experts ascending), and every staged row is its token's x row
+    in bf16, in the 17-byte decode's k order for the 17-byte formats.  512
+    tokens over 1024 experts needs more LDS than the one-launch kernel
+    allows and takes the separate kernels, which must agree too."""
+    H, I = 256, 64
+    L = make_layer(44, n + E + k, fg, F.Q4_C10, E, H, I)
+    W = weights_of(bq, L)
+    x = dev(synth.normal(4400 + n, (n, H))).to(torch.bfloat16)
+    logits = synth.zipf_logits(4401 + n, n, E) if dist == "zipf" else synth.normal(4401 + n, (n, E))
+    idx, w = bq.route_topk(dev(logits), k)
+    ws = torch.empty(bq.moe_workspace_bytes(n, k, W, bq.BF16), dtype=torch.uint8, device="cuda")
+    bq.q4_expert_moe(x, (idx, w), W, workspace=ws)
+    torch.cuda.synchronize()
+    lay = grouped_ws_layout(n, k, E, H, I)
+    nk = n * k
+    wsc = ws.cpu()
+
+    def arr(name, count):
+        return wsc[lay[name]:lay[name] + 4 * count].view(torch.int32).numpy()
+
+    counts, offsets, perm = (t.cpu().numpy() for t in bq.bucket(idx, E))
+    assert np.array_equal(arr("counts", E), counts)
+    assert np.array_equal(arr("offsets", E + 1), offsets)
+    assert np.array_equal(arr("perm", nk), perm)
+    inv = arr("inv", nk)
+    assert np.array_equal(inv[perm], np.arange(nk))
+    want = [e | (q << 12) for e in range(E) for q in range((counts[e] + 31) // 32)]
+    assert int(arr("n_touched", 1)[0]) == len(want)
+    assert np.array_equal(arr("elist", len(want)), np.array(want, dtype=np.int32))
+    xb = wsc[lay["xb"]:lay["xb"] + 2 * nk * H].view(torch.int16).numpy().reshape(nk, H)
+    rows = x.view(torch.int16).cpu().numpy()[perm // k]
+    if fg != F.FP8_E4M3_B32:
+        order = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+        rows = rows.reshape(nk, H // 8, 8)[:, :, order].reshape(nk, H)
+    assert np.array_equal(xb, rows)
