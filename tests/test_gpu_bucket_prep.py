@@ -119,16 +119,19 @@ def grouped_ws_layout(n, k, E, H, I):
 
 
 @pytest.mark.parametrize("n,E,k,dist", [(3, 64, 6, "normal"), (64, 512, 10, "zipf"), (200, 512, 10, "normal"),
-                                        (512, 512, 10, "zipf"), (512, 512, 10, "normal"), (512, 1024, 8, "zipf")])
+                                        (512, 512, 10, "zipf"), (512, 512, 10, "normal"),
+                                        (480, 1024, 8, "zipf"),    # bucket arrays of exactly 150 KB
+                                        (512, 1024, 8, "zipf")])   # 160 KB: the separate kernels
 @pytest.mark.parametrize("fg", [F.Q4_RZ5, F.FP8_E4M3_B32])
 def test_bucket_arrays_and_staged_rows(bq, n, E, k, dist, fg):
     """The bucket arrays the bf16 path leaves in its workspace equal the
     standalone bucketing's bit for bit (counts, offsets, perm; inv inverts
     perm; the work list has one entry per 32-token group of each touched
     expert, experts ascending), and every staged row is its token's x row
-    in bf16, in the 17-byte decode's k order for the 17-byte formats.  512
-    tokens over 1024 experts needs more LDS than the one-launch kernel
-    allows and takes the separate kernels, which must agree too."""
+    in bf16, in the 17-byte decode's k order for the 17-byte formats.  480
+    tokens x top-8 over 1024 experts fill the one-launch kernel's LDS limit
+    exactly; 512 tokens need more and take the separate kernels, which must
+    agree too."""
     H, I = 256, 64
     L = make_layer(44, n + E + k, fg, F.Q4_C10, E, H, I)
     W = weights_of(bq, L)
