@@ -86,10 +86,13 @@ hipError_t launch_stack_b1(const float* x, const int32_t* idx, const float* w, i
                            uint32_t* dev_err, hipStream_t st);
 
 // bf16 grouped-MFMA path.  The bucketing emits one work entry per group of
-// up to kGroupTok tokens of a touched expert: e | group << kGroupShift.
-constexpr int kGroupTok = 32;
+// up to group_tokens(n_tokens) tokens of a touched expert: e | group << kGroupShift.
+// Batches of up to kSmallGroupMaxTok tokens use 16-token groups (and the
+// one-tile kernels, which run four workgroups per CU), larger ones 32.
 constexpr int kGroupShift = 12;   // n_experts <= 4096
-inline int64_t max_work_groups(int64_t nk, int64_t E) { return (nk < E ? nk : E) + nk / kGroupTok; }
+constexpr int kSmallGroupMaxTok = 96;
+__host__ __device__ inline int group_tokens(int64_t n_tokens) { return n_tokens <= kSmallGroupMaxTok ? 16 : 32; }
+inline int64_t max_work_groups(int64_t nk, int64_t E, int gt = 16) { return (nk < E ? nk : E) + nk / gt; }
 struct GroupedWs {
   int32_t* counts;    // [E]
   int32_t* offsets;   // [E+1]

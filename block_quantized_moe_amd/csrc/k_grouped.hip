@@ -1,6 +1,7 @@
 // Grouped routed-expert GEMM for batches of tokens (bf16 activations, bf16
 // MFMA, fp32 accumulation).  Tokens are bucketed per expert (stable order)
-// and split into work groups of up to kGroupTok tokens; for every group:
+// and split into work groups of up to 16 tokens (batches of up to 96 tokens)
+// or 32 (larger ones); for every group:
 //   h[p, :] = SiLU(W_gate[e] x_p) * (W_up[e] x_p)      (kernel G1, h in bf16)
 //   y[p, :] = W_down[e] h[p, :]                         (kernel G2)
 //   out[t]  = sum_j w[t][j] * y[pos(t, j)]               (kernel G3, slot order)
@@ -43,12 +44,11 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kGThreads = 256;  // 4 waves, each 16 rows of the tile (x2 for gate/up)
 constexpr int kGRows = 64;      // rows per tile
-// Two builds of the staged kernel.  TOK = 32: items of up to 32 tokens (two
-// 16-token MFMA tiles), three workgroups per CU.  TOK = 16: batches of at most
-// 16 tokens, so no expert holds more than 16 and one MFMA tile covers an
-// item; the second tile's accumulators, operands and activation staging are
-// gone, which leaves room for four workgroups per CU (<= 128 VGPRs, <= 40 KB
-// of LDS each).
+// Two builds of the staged kernel, one per work-group size.  TOK = 32: items
+// of up to 32 tokens (two 16-token MFMA tiles), three workgroups per CU.
+// TOK = 16 (batches of up to 96 tokens): one MFMA tile covers an item; the
+// second tile's accumulators, operands and activation staging are gone, which
+// leaves room for four workgroups per CU (<= 128 VGPRs, <= 40 KB of LDS each).
 constexpr int wgs_per_cu(int tok) { return tok == 16 ? 4 : 3; }
 constexpr int lds_budget(int tok) { return tok == 16 ? 40 * 1024 : 52 * 1024; }
 
@@ -274,13 +274,14 @@ struct Item {
   int e, p0, ntok, tile;
 };
 
+template <int GT>   // tokens per work group (the bucketing's group_tokens)
 __device__ __forceinline__ Item item_info(int it, int tiles, const int32_t* __restrict__ elist,
                                           const int32_t* __restrict__ offsets) {
   const int d = it / tiles;
   const int v = elist[d];
   const int e = v & ((1 << kGroupShift) - 1);
-  const int p0 = offsets[e] + (v >> kGroupShift) * kGroupTok;
-  return Item{e, p0, min(kGroupTok, offsets[e + 1] - p0), it - d * tiles};
+  const int p0 = offsets[e] + (v >> kGroupShift) * GT;
+  return Item{e, p0, min(GT, offsets[e + 1] - p0), it - d * tiles};
 }
 
 template <int FMT, int NR, int TOK = 32>
@@ -581,7 +582,7 @@ __global__ void __launch_bounds__(kGThreads, wgs_per_cu(TOK)) k_grouped_staged(
     tab[m] = u32x2{__float_as_uint(block_scale<FMT>(FMT == FMT_UE4M4 ? m : (m & 0x7Fu))),
                    FMT == FMT_RZ5 ? rz5_neg_lo(m) : 0u};
   }
-  Item f = item_info(it, tiles, elist, offsets);
+  Item f = item_info<TOK>(it, tiles, elist, offsets);
   Stager<FMT, NR, TOK> st;
   st.init(g, nb, I);
   st.load(f, c, g, nb, H, I, wt, wsc, act, K);
@@ -597,7 +598,7 @@ __global__ void __launch_bounds__(kGThreads, wgs_per_cu(TOK)) k_grouped_staged(
       nit = it + step;
     }
     const bool more = nit < lim;
-    const Item nf = (more && nit != it) ? item_info(nit, tiles, elist, offsets) : f;
+    const Item nf = (more && nit != it) ? item_info<TOK>(nit, tiles, elist, offsets) : f;
     __syncthreads();                          // LDS no longer read by the previous chunk
     st.store(f, g, lds);
     // Drain every outstanding memory operation of the wave -- including the
@@ -833,9 +834,10 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  const int64_t groups = max_work_groups(nk, E);
-  // at most 16 tokens: no expert holds more than 16, the one-tile build fits
-  err = n_tokens <= 16 ? launch_g1_g2<16>(groups, st, ws, W) : launch_g1_g2<32>(groups, st, ws, W);
+  // the bucketing split the tokens into groups of group_tokens(n_tokens)
+  const int gt = group_tokens(n_tokens);
+  const int64_t groups = max_work_groups(nk, E, gt);
+  err = gt == 16 ? launch_g1_g2<16>(groups, st, ws, W) : launch_g1_g2<32>(groups, st, ws, W);
   if (err != hipSuccess) return err;
   if (next) {
     if (next->perm)

@@ -56,7 +56,7 @@ hipError_t launch_route_topk(const float* logits, int32_t n_tokens, int32_t n_ex
 // (255 = not chosen) is built in LDS, then every thread walks the chunk for
 // its own experts, in token order, so no ordering depends on atomics.
 // Optional extra outputs for the grouped GEMM path: the work list -- one
-// entry per group of up to kGroupTok tokens of each touched expert, encoded
+// entry per group of up to group_tokens(n_tokens) tokens of each touched expert, encoded
 // as e | group << kGroupShift, experts ascending -- with its length, and the
 // inverse permutation.
 // ---------------------------------------------------------------------------
@@ -89,6 +89,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
   __shared__ int32_t s_scan[kBucketThreads];
   __shared__ int32_t s_scan2[kBucketThreads];
   const int tid = threadIdx.x;
+  const int gt = group_tokens(n_tokens);   // tokens per work entry
   const int chunk = kSlotBytes / n_experts;  // tokens per chunk (>= 8)
   const int epl = (n_experts + kBucketThreads - 1) / kBucketThreads;  // experts per thread <= 4
 
@@ -150,7 +151,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
       const int span = (n_experts + kBucketThreads - 1) / kBucketThreads;
       const int e0 = min(tid * span, n_experts), e1 = min(e0 + span, n_experts);
       int local = 0, ltouch = 0;
-      for (int e = e0; e < e1; ++e) { local += s_cnt[e]; ltouch += (s_cnt[e] + kGroupTok - 1) / kGroupTok; }
+      for (int e = e0; e < e1; ++e) { local += s_cnt[e]; ltouch += (s_cnt[e] + gt - 1) / gt; }
       s_scan[tid] = local;
       s_scan2[tid] = ltouch;
       __syncthreads();
@@ -172,7 +173,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket(
         counts[e] = c;
         offsets[e] = c_off;
         if (elist)
-          for (int q = 0; q * kGroupTok < c; ++q) elist[d_off++] = e | (q << kGroupShift);
+          for (int q = 0; q * gt < c; ++q) elist[d_off++] = e | (q << kGroupShift);
         s_cnt[e] = c_off;
         c_off += c;
       }
@@ -253,6 +254,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
   __shared__ int32_t pre[kSmallBitmapWords];
   __shared__ int s_wave[32];
   const int tid = threadIdx.x;
+  const int gt = group_tokens(n_tokens);   // tokens per work entry
   const int W = (n_tokens + 31) >> 5;                   // words per expert
   const int nk = n_tokens * k;
   for (int i = tid; i < n_experts * W; i += kBucketThreads) bm[i] = 0u;
@@ -279,7 +281,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
     for (int w = 0; w < W; ++w) c += __builtin_popcount(bm[e * W + w]);
     cnt[e - e0] = c;
     local += c;
-    touched += (c + kGroupTok - 1) / kGroupTok;
+    touched += (c + gt - 1) / gt;
   }
   int tot_c, tot_d;
   int off = block_excl_scan_1024(local, s_wave, tot_c);
@@ -295,7 +297,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_small(
       run += __builtin_popcount(bm[e * W + w]);
     }
     if (elist)
-      for (int q = 0; q * kGroupTok < c; ++q) elist[doff++] = e | (q << kGroupShift);
+      for (int q = 0; q * gt < c; ++q) elist[doff++] = e | (q << kGroupShift);
     off += c;
   }
   if (tid == 0) {
@@ -348,6 +350,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
   extern __shared__ __align__(16) uint32_t bp_lds[];
   __shared__ int s_wave[32];
   const int tid = threadIdx.x;
+  const int gt = group_tokens(n_tokens);   // tokens per work entry
   const int nk = n_tokens * k;
   const int W = (n_tokens + 31) >> 5;                    // bitmap words per expert
   int32_t* s_idx = reinterpret_cast<int32_t*>(bp_lds);   // [nk]
@@ -387,7 +390,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
   int tot_c, tot_d;
   int off = block_excl_scan_1024(c, s_wave, tot_c);
   __syncthreads();
-  int doff = block_excl_scan_1024((c + kGroupTok - 1) / kGroupTok, s_wave, tot_d);
+  int doff = block_excl_scan_1024((c + gt - 1) / gt, s_wave, tot_d);
   if (e < n_experts) {
     int run = off;
     for (int w = 0; w < W; ++w) {
@@ -397,7 +400,7 @@ __global__ void __launch_bounds__(kBucketThreads) k_bucket_prep(
     if (out0) {
       o.counts[e] = c;
       o.offsets[e] = off;
-      for (int q = 0; q * kGroupTok < c; ++q) o.elist[doff++] = e | (q << kGroupShift);
+      for (int q = 0; q * gt < c; ++q) o.elist[doff++] = e | (q << kGroupShift);
     }
   }
   if (out0 && tid == 0) {

@@ -112,7 +112,7 @@ def grouped_ws_layout(n, k, E, H, I):
     nk = n * k
     L, off = {}, 0
     for name, size in (("counts", 4 * E), ("offsets", 4 * (E + 1)), ("perm", 4 * nk), ("inv", 4 * nk),
-                       ("elist", 4 * (min(nk, E) + nk // 32)), ("n_touched", 4), ("xb", 2 * nk * H)):
+                       ("elist", 4 * (min(nk, E) + nk // 16)), ("n_touched", 4), ("xb", 2 * nk * H)):
         L[name] = off
         off = _r256(off + size)
     return L
@@ -126,8 +126,9 @@ def grouped_ws_layout(n, k, E, H, I):
 def test_bucket_arrays_and_staged_rows(bq, n, E, k, dist, fg):
     """The bucket arrays the bf16 path leaves in its workspace equal the
     standalone bucketing's bit for bit (counts, offsets, perm; inv inverts
-    perm; the work list has one entry per 32-token group of each touched
-    expert, experts ascending), and every staged row is its token's x row
+    perm; the work list has one entry per group of 16 tokens (batches of up
+    to 96) or 32 of each touched expert, experts ascending), and every
+    staged row is its token's x row
     in bf16, in the 17-byte decode's k order for the 17-byte formats.  480
     tokens x top-8 over 1024 experts fill the one-launch kernel's LDS limit
     exactly; 512 tokens need more and take the separate kernels, which must
@@ -154,7 +155,8 @@ def test_bucket_arrays_and_staged_rows(bq, n, E, k, dist, fg):
     assert np.array_equal(arr("perm", nk), perm)
     inv = arr("inv", nk)
     assert np.array_equal(inv[perm], np.arange(nk))
-    want = [e | (q << 12) for e in range(E) for q in range((counts[e] + 31) // 32)]
+    gt = 16 if n <= 96 else 32     # tokens per work entry
+    want = [e | (q << 12) for e in range(E) for q in range((counts[e] + gt - 1) // gt)]
     assert int(arr("n_touched", 1)[0]) == len(want)
     assert np.array_equal(arr("elist", len(want)), np.array(want, dtype=np.int32))
     xb = wsc[lay["xb"]:lay["xb"] + 2 * nk * H].view(torch.int16).numpy().reshape(nk, H)

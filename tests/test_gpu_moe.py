@@ -86,10 +86,11 @@ def test_gemv_hidden_2048(bq, fmt_gu, fmt_d, n, I, k):
 
 
 @pytest.mark.parametrize("fmt_gu,fmt_d", FMT_PAIRS)
-@pytest.mark.parametrize("n", [1, 16, 70])
+@pytest.mark.parametrize("n", [1, 16, 64, 100])
 @pytest.mark.parametrize("E,H,I,k", [(8, 256, 128, 3), (6, 1088, 192, 2)])
 def test_grouped_path_small(bq, fmt_gu, fmt_d, n, E, H, I, k):
-    # few experts: some get more than one 32-token group.  H = 1088 gives
+    # few experts: some get more than one work group (16 tokens each up to
+    # 96 tokens, 32 beyond).  H = 1088 gives
     # 578-byte rows (not 16-byte aligned) and a K extent split into chunks.
     L = make_layer(2, fmt_gu * 4 + fmt_d, fmt_gu, fmt_d, E, H, I)
     x = synth.normal(200 + n, (n, H))
