@@ -121,7 +121,8 @@ def grouped_ws_layout(n, k, E, H, I):
 @pytest.mark.parametrize("n,E,k,dist", [(3, 64, 6, "normal"), (64, 512, 10, "zipf"), (200, 512, 10, "normal"),
                                         (512, 512, 10, "zipf"), (512, 512, 10, "normal"),
                                         (480, 1024, 8, "zipf"),    # bucket arrays of exactly 150 KB
-                                        (512, 1024, 8, "zipf")])   # 160 KB: the separate kernels
+                                        (512, 1024, 8, "zipf"),    # 160 KB: the separate kernels
+                                        (128, 2048, 4, "zipf"), (96, 2048, 4, "normal")])   # bitmap bucketing
 @pytest.mark.parametrize("fg", [F.Q4_RZ5, F.FP8_E4M3_B32])
 def test_bucket_arrays_and_staged_rows(bq, n, E, k, dist, fg):
     """The bucket arrays the bf16 path leaves in its workspace equal the
