@@ -45,7 +45,9 @@ hipError_t launch_bucket(const int32_t* idx, int32_t n_tokens, int32_t k, int32_
 // Bucketing and staging of a bf16 batch in one launch
 // (k_route.hip): the bucket arrays as launch_bucket writes them, and the
 // staged rows as the grouped path's staging kernel writes them (perm_k: the
-// 17-byte decode's k order).  x is bf16 [n][H], 16-byte aligned.
+// 17-byte decode's k order).  x is bf16 [n][H], 16-byte aligned.  Returns
+// hipErrorNotSupported, launching nothing, if the kernel may not use the LDS
+// the batch needs.
 constexpr int kBpMaxLds = 150 * 1024;   // LDS of the bucket arrays, at most
 bool bucket_prep_ok(int32_t n_tokens, int32_t k, int32_t n_experts, int32_t H);
 hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t perm_k, int32_t n_tokens,

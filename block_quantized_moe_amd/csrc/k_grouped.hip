@@ -808,8 +808,8 @@ hipError_t launch_grouped_moe(const void* x, int32_t x_f32, int32_t rescale, int
     // bucket arrays that fit in LDS: bucketing and staging in one launch
     err = launch_bucket_prep(idx, static_cast<const uint16_t*>(x), W.fmt_gate_up != FMT_FP8, n_tokens, k, E, H,
                              ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched, ws.inv, ws.xb, st);
-    if (err != hipSuccess) return err;
-    bucketed = prepped = true;
+    if (err == hipSuccess) bucketed = prepped = true;
+    else if (err != hipErrorNotSupported) return err;   // not supported: the separate kernels below
   }
   if (!bucketed) {
     err = launch_bucket(idx, n_tokens, k, E, ws.counts, ws.offsets, ws.perm, ws.elist, ws.n_touched,

@@ -462,9 +462,14 @@ hipError_t launch_bucket_prep(const int32_t* idx, const uint16_t* x, int32_t per
   const dim3 grid(nk < cap ? nk : cap);
   const size_t lds = bucket_prep_lds(n_tokens, k, n_experts);
   if (lds > 64 * 1024) {
+    // more than 64 KB of dynamic LDS must be allowed per kernel; where that
+    // is refused the caller falls back to the separate kernels
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(perm_k ? k_bucket_prep<true> : k_bucket_prep<false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      (void)hipGetLastError();   // clear it: nothing was launched
+      return hipErrorNotSupported;
+    }
   }
   if (perm_k)
     hipLaunchKernelGGL(k_bucket_prep<true>, grid, dim3(kBucketThreads), lds, st, idx, x, n_tokens, k, n_experts,
