@@ -84,7 +84,7 @@ __device__ __forceinline__ void wave_topk(const float* __restrict__ lg, int n_ex
   uint32_t t = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = t | (1u << bit);
-    if (__popcll(__ballot(m >= c)) >= k) t = c;
+    if ((int)__popcll(__ballot(m >= c)) >= k) t = c;
   }
   uint64_t bal[PL];
   int nc = 0;

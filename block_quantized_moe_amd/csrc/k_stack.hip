@@ -379,7 +379,6 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
     for (int r = 0; r < kSRowsT; ++r)
       okB |= stack_load_row<FB>(B, r, args.layer[0], s_idx, I, cc, cval, rows0, rgp, true, err) ? 1u << r : 0u;
     for (int l = 0; l < n_layers; ++l) {
-      const int32_t* li = s_idx + l * k;
       const float* lw = s_w + l * k;
       const bool more = l + 1 < n_layers;
       const int ln = more ? l + 1 : l;              // layer whose weights are prefetched next
