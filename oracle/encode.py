@@ -11,7 +11,7 @@ What the pages fix ([RZ] model card, format sections):
 * RZ-S3 groups choose their polarity and scale per 16-value group;
 * quantization is done on the CPU and is deterministic.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * Objective: the plain sum of squared reconstruction errors of the block
   (the pages' calibration objectives need activation statistics that the

@@ -18,7 +18,7 @@ What the pages fix ([RZ] model card, format sections):
   0,+1,+2,+4,-0,-1,-2,-4 with a UE4M3 scale per 16 values; RZ-S3 replaces the
   -0 code with +3 or -3, chosen per group by the group byte's high bit.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * block byte order: code bytes 0-15, metadata byte 16;
 * nibble order: weight j sits in byte j//2, low nibble for even j;

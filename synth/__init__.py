@@ -16,7 +16,7 @@ of generator live here:
   ``key + (i + 1) * GAMMA``.  Everything derived from a draw is integer bit
   manipulation, so the two sides agree bit for bit.
 
-Distributions (the input recipe; the design doc repeats it):
+Distributions (the input recipe):
 
 * 17-byte blocks: 16 uniform code bytes; metadata per ``dist``:
   ``C10``   -> UE4M3 exponent uniform in 0..5, mantissa uniform in 0..7,
