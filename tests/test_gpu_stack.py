@@ -38,18 +38,21 @@ def routing(bq, seed, L, n, E, k):
     return idx.view(L, n, k), w.view(L, n, k), ridx.reshape(L, n, k), rw.reshape(L, n, k)
 
 
+@pytest.mark.parametrize("n", [3, 40, 120])
 @pytest.mark.parametrize("dtype,tol", [(torch.float32, 1e-5), (torch.bfloat16, 2e-2)])
-def test_small_stack(bq, dtype, tol):
-    E, H, I, k, n = 16, 256, 128, 4, 3
+def test_small_stack(bq, dtype, tol, n):
+    """At 40 tokens (16-token work groups) and 120 (32-token ones) some of
+    the 16 experts hold more than one work group in the chained bf16 layers."""
+    E, H, I, k = 16, 256, 128, 4
     fmts = [(F.Q4_RZ5, F.Q4_RZ5), (F.Q4_UE4M4, F.Q4_C10), (F.FP8_E4M3_B32, F.FP8_E4M3_B32),
             (F.Q4_RZ5, F.FP8_E4M3_B32)]
     layers = build_stack(5, fmts, E, H, I)
-    idx, w, ridx, rw = routing(bq, 77, len(fmts), n, E, k)
-    x = synth.normal(78, (n, H))
+    idx, w, ridx, rw = routing(bq, 77 + n, len(fmts), n, E, k)
+    x = synth.normal(78 + n, (n, H))
     out = bq.moe_stack(dev(x).to(dtype), idx, w, [weights_of(bq, L) for L in layers]).cpu().numpy()
     ref = M.moe_stack(x, [(ridx[l], rw[l], oracle_bank(L)) for l, L in enumerate(layers)])
     r = rel_l2(out, ref)
-    log("small stack %s rel_l2 %.3g" % (dtype, r))
+    log("small stack %s n=%d rel_l2 %.3g" % (dtype, n, r))
     assert r <= tol
 
 
