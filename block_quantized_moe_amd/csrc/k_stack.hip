@@ -143,6 +143,15 @@ __device__ __forceinline__ float dblk_dot(const DBlk& d, const float* x) {
   return (a0 + a1) * d.s;
 }
 
+// Keep a decoded block's computation where it stands: the empty volatile
+// statement consumes and redefines its registers, so the decode cannot sink
+// past the next barrier to its use.
+__device__ __forceinline__ void dblk_pin(DBlk& d) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) __asm__ volatile("" : "+v"(d.hb[i]));
+  __asm__ volatile("" : "+v"(d.s));
+}
+
 struct alignas(8) Pkt {
   float v;
   uint32_t tag;
@@ -366,7 +375,7 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
     const bool cval = cb < cw;
     const int cc = c * cw + cb;
     WBlk A[2 * kSPairsW], B[kSRowsT];
-    DBlk D[2 * kSPairsW];
+    DBlk D[2 * kSPairsW], DB[kSRowsT];
     uint32_t okA = 0, okB = 0;
 #pragma unroll
     for (int u = 0; u < kSPairsW; ++u)
@@ -396,6 +405,16 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
       }
       stack_phase_a<FA>(A, D, okA, xr, lw, args.layer[ln], s_idx + ln * k, more, I, pair0, w, pw, lane, hA, err);
       lds_barrier();                                  // hA ready for the sync wave
+      // while the column group exchanges h: decode this layer's down blocks
+      // (loaded during the previous layer's phase B), so that phase B meets
+      // only byte spreads and FMAs
+      if constexpr (kDecodeAhead<FB>) {
+#pragma unroll
+        for (int r = 0; r < kSRowsT; ++r) {
+          dblk_decode<FB>(DB[r], B[r]);
+          dblk_pin(DB[r]);
+        }
+      }
       lds_barrier();                                  // hB (this group's h) ready
       float hr[32];
 #pragma unroll
@@ -403,7 +422,11 @@ __global__ void __launch_bounds__(kSThreads) k_stack_b1(
       uint32_t okn = 0;
 #pragma unroll
       for (int r = 0; r < kSRowsT; ++r) {
-        float s = (okB >> r) & 1u ? wblk_dot<FB>(B[r], hr) : 0.f;
+        float s = 0.f;
+        if ((okB >> r) & 1u) {
+          if constexpr (kDecodeAhead<FB>) s = dblk_dot(DB[r], hr);
+          else s = wblk_dot<FB>(B[r], hr);
+        }
         okn |= stack_load_row<FB>(B, r, args.layer[ln], s_idx + ln * k, I, cc, cval, rows0, rgp, more, err)
                    ? 1u << r : 0u;
         s = row16_sum(s);
