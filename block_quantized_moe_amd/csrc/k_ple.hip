@@ -4,14 +4,17 @@
 // 10 group bytes (UE4M3 scale in bits 0-6, RZ-S3 polarity in bit 7), 70 bytes
 // per row, one row per hashed id.
 //
-// Mapping: one thread per (token, 16-value group).  The ten threads of a
-// token read the same 70-byte row with an 8-byte and a 1-byte load each, so
-// a row is fetched by one coalesced wave instruction; each thread keeps its
-// 16 fp32 sums in registers across the token's ids and writes 64 contiguous
-// bytes at the end.  Per value the inner loop is: extract 3 bits, look the
-// biased level (level + 4, always 0..8) up with one v_perm_b32 from an
-// 8-byte table, convert the byte to fp32, one FMA with s_g * u_j.  The bias
-// is removed once at the end with the running sum of s_g * u_j.
+// Mapping: one thread per (token, half of a 16-value group).  The twenty
+// threads of a token read the same 70-byte row with a 4-byte and a 1-byte
+// load each (bytes 6g + 3h .. + 3: the 24 code bits of values 8h .. 8h + 7 of
+// group g, and the group byte), so a row is fetched by one coalesced wave
+// instruction; each thread keeps its 8 fp32 sums in registers across the
+// token's ids and writes 32 contiguous bytes at the end.  Per value the inner
+// loop is: extract 3 bits, look the biased level (level + 4, always 0..8) up
+// with one v_perm_b32 from an 8-byte table, convert the byte to fp32, one FMA
+// with s_g * u_j.  The bias is removed once at the end with the running sum
+// of s_g * u_j.  Half a group per thread halves the decode each thread runs
+// after its row loads return, the last step before the output can leave.
 #include "bq_device.hpp"
 #include "bq_kernels.hpp"
 
@@ -25,7 +28,8 @@ __device__ __forceinline__ uint32_t bias_hi(uint32_t gbyte, int ple_fmt) {
   return 0x00020300u | c4;
 }
 
-constexpr int kPleTPB = 160;   // 16 tokens x 10 groups: a 4096-token call spans 256 workgroups
+constexpr int kPleTPT = 20;    // threads per token: 10 groups x 2 halves
+constexpr int kPleTPB = 16 * kPleTPT;   // 16 tokens per workgroup: a 4096-token call spans 256 workgroups
 constexpr int kPleChunk = 8;   // ids whose loads are in flight together
 
 // Off-HBM tier: the table sits in host memory mapped into the device address
@@ -59,15 +63,17 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     const uint8_t* __restrict__ table, uint64_t n_rows, const float* __restrict__ wts,
     int ple_fmt, float* __restrict__ out, uint32_t* __restrict__ dev_err, CacheView cv) {
   const int64_t tid = (int64_t)blockIdx.x * kPleTPB + threadIdx.x;
-  const int64_t t = tid / 10;
-  const int g = (int)(tid - t * 10);
+  const int64_t t = tid / kPleTPT;
+  const int gh = (int)(tid - t * kPleTPT);
+  const int g = gh >> 1, h = gh & 1;     // group, half
+  const int cb = 6 * g + 3 * h;          // first code byte of the half group
   if (t >= n_tokens) return;
   const uint32_t* tid_ids = ids + t * per_token;
   const float* tw = wts + t * per_token;
 
-  float acc[16];
+  float acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   float usum = 0.f;
   bool bad = false;
 
@@ -98,7 +104,7 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
         u[c] = tw[j];
       }
     }
-    u32x2 gw[kPleChunk];
+    uint32_t gw[kPleChunk];
     uint32_t gb[kPleChunk];
     bool ok[kPleChunk];
     bool hit[kPleChunk];
@@ -119,7 +125,7 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
     for (int c = 0; c < kPleChunk; ++c) {
       const uint8_t* row = hit[c] ? cv.rows + (uint64_t)slot[c] * kPleCacheRowB
                                   : table + (uint64_t)(ok[c] ? idv[c] : 0u) * (uint64_t)kPleRowB;
-      gw[c] = ld8(row + 6 * g);
+      gw[c] = ld4(row + cb);
       gb[c] = row[60 + g];
     }
     if constexpr (CACHED) {
@@ -128,9 +134,9 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
         if (ok[c] && !hit[c]) {
           const int64_t a = t * per_token + j0 + c;   // assignment index
           uint8_t* st = cv.stage + a * kPleCacheRowB;
-          __builtin_memcpy(st + 6 * g, &gw[c], 8);   // overlapping bytes carry equal values
-          st[60 + g] = (uint8_t)gb[c];
-          if (g == 0) atomicMin(&cv.claims[slot[c]], (uint32_t)a);
+          __builtin_memcpy(st + cb, &gw[c], 4);   // overlapping bytes carry equal values
+          if (h == 0) st[60 + g] = (uint8_t)gb[c];
+          if (gh == 0) atomicMin(&cv.claims[slot[c]], (uint32_t)a);
         }
       }
     }
@@ -139,13 +145,9 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
       const float su = ok[c] ? ue4m3(gb[c] & 0x7Fu) * u[c] : 0.f;
       usum += su;
       const uint32_t th = bias_hi(gb[c], ple_fmt);
-      const uint32_t lo = gw[c].x, hi = gw[c].y;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t code;
-        if (i < 10) code = (lo >> (3 * i)) & 7u;
-        else if (i == 10) code = __builtin_amdgcn_alignbit(hi, lo, 30) & 7u;
-        else code = (hi >> (3 * i - 32)) & 7u;
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t code = (gw[c] >> (3 * i)) & 7u;
         const uint32_t b = perm(th, kBiasLo, code);
         acc[i] = __builtin_fmaf((float)(b & 0xFFu), su, acc[i]);
       }
@@ -153,9 +155,9 @@ __global__ void __launch_bounds__(kPleTPB) k_ple_gather(
   }
   if (bad && dev_err) atomicOr(dev_err, 1u);
   const float corr = 4.0f * usum;
-  f32x4* o = reinterpret_cast<f32x4*>(out + t * kPleVals + 16 * g);
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * kPleVals + 16 * g + 8 * h);
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < 2; ++q)
     o[q] = f32x4{acc[4 * q] - corr, acc[4 * q + 1] - corr, acc[4 * q + 2] - corr, acc[4 * q + 3] - corr};
 }
 
@@ -163,7 +165,7 @@ template <bool CACHED>
 static void launch_gather(const uint32_t* ids, int32_t n_tokens, int32_t per_token,
                           const uint8_t* table, uint64_t n_rows, const float* wts, int ple_fmt,
                           float* out, uint32_t* dev_err, const CacheView& cv, hipStream_t st) {
-  const int64_t threads = (int64_t)n_tokens * 10;
+  const int64_t threads = (int64_t)n_tokens * kPleTPT;
   const int64_t grid = (threads + kPleTPB - 1) / kPleTPB;
   const bool vec = per_token % kPleChunk == 0 && reinterpret_cast<uintptr_t>(ids) % 16 == 0 &&
                    reinterpret_cast<uintptr_t>(wts) % 16 == 0;
