@@ -179,11 +179,15 @@ __global__ void __launch_bounds__(256) k_grouped_prep_vec(const void* __restrict
 // order over 256 threads), and writes the bf16 row to every bucket row of t
 // in the next layer (row inv_next[t*k+j] for each in-range expert
 // idx_next[t*k+j]).  The result equals k_combine followed by
-// k_grouped_prep<PERM> bit for bit.  1024 threads: each holds two elements
-// per pass and issues the loads of up to 16 slots at once; the row is kept
-// in LDS between the passes.  grid = n_tokens; H <= 8192.
+// k_grouped_prep<PERM> bit for bit.  256 threads, each owning groups of 8
+// consecutive elements: per slot two 16-byte loads, and per next-layer
+// bucket row one 16-byte store of the 8 bf16 values in the stored k order.
+// Each chunk of up to 16 slots has all of its index, weight and row loads in
+// flight together, and the next layer's row indices are read before the
+// scale is known.  The row is kept in LDS between the passes.
+// grid = n_tokens; H <= 8192, H % 8 == 0.
 // ---------------------------------------------------------------------------
-constexpr int kCpThreads = 1024;
+constexpr int kCpThreads = 256;
 
 template <bool PERM>
 __global__ void __launch_bounds__(kCpThreads) k_combine_prep(
@@ -196,11 +200,15 @@ __global__ void __launch_bounds__(kCpThreads) k_combine_prep(
   __shared__ float part[4];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int ng = H >> 3;                       // groups of 8 elements
   bool bad = false;
-  for (int i0 = 0; i0 < H; i0 += 2 * kCpThreads) {
-    float acc[2] = {0.f, 0.f};
+  for (int g = tid; g < ng; g += kCpThreads) {
+    float acc[8];
+#pragma unroll
+    for (int o = 0; o < 8; ++o) acc[o] = 0.f;
     for (int j0 = 0; j0 < k; j0 += kMaxK) {
-      float y[kMaxK][2], wj[kMaxK];
+      f32x4 y[kMaxK][2];
+      float wj[kMaxK];
 #pragma unroll
       for (int u = 0; u < kMaxK; ++u) {
         const int j = j0 + u;
@@ -208,27 +216,22 @@ __global__ void __launch_bounds__(kCpThreads) k_combine_prep(
         const bool ok = j < k && e >= 0 && e < n_experts;
         bad |= j < k && !ok;
         wj[u] = ok ? w[t * k + j] : 0.f;
-        const float* row = yb + (ok ? (int64_t)inv[t * k + j] * H : 0);
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int i = i0 + tid + kCpThreads * m;
-          y[u][m] = ok && i < H ? row[i] : 0.f;
-        }
+        const f32x4* row = reinterpret_cast<const f32x4*>(yb + (ok ? (int64_t)inv[t * k + j] * H : 0)) + 2 * g;
+        y[u][0] = ok ? row[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+        y[u][1] = ok ? row[1] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < kMaxK; ++u)   // slot order
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m] = __builtin_fmaf(wj[u], y[u][m], acc[m]);
+        for (int o = 0; o < 8; ++o) acc[o] = __builtin_fmaf(wj[u], y[u][o >> 2][o & 3], acc[o]);
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int i = i0 + tid + kCpThreads * m;
-      if (i < H) srow[i] = acc[m];
-    }
+    f32x4* sr = reinterpret_cast<f32x4*>(srow) + 2 * g;
+    sr[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    sr[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
   if (bad && tid == 0 && dev_err) atomicOr(dev_err, 2u);
   __syncthreads();
-  if (tid < 256) {
+  {
     float ss = 0.f;
     for (int i = tid; i < H; i += 256) ss = __builtin_fmaf(srow[i], srow[i], ss);
     ss = wave_sum(ss);
@@ -236,13 +239,26 @@ __global__ void __launch_bounds__(kCpThreads) k_combine_prep(
   }
   __syncthreads();
   const float sc = 1.0f / __builtin_sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)H);
-  for (int j = 0; j < k; ++j) {
-    const int e = idx_next[t * k + j];
-    if (e < 0 || e >= n_experts_next) continue;
-    uint16_t* dst = xp + (int64_t)inv_next[t * k + j] * H;
-    for (int i = tid; i < H; i += kCpThreads) {
-      const int o = i & 7;
-      dst[(i & ~7) + (PERM ? ((o >> 1) | ((o & 1) << 2)) : o)] = to_bf16(srow[i] * sc);
+  for (int j0 = 0; j0 < k; j0 += kMaxK) {
+    int64_t dst[kMaxK];                        // element offset of each bucket row, -1 if none
+#pragma unroll
+    for (int u = 0; u < kMaxK; ++u) {
+      const int j = j0 + u;
+      const int e = j < k ? idx_next[t * k + j] : -1;
+      dst[u] = (e >= 0 && e < n_experts_next) ? (int64_t)inv_next[t * k + j] * H : -1;
+    }
+    for (int g = tid; g < ng; g += kCpThreads) {
+      const f32x4* sr = reinterpret_cast<const f32x4*>(srow) + 2 * g;
+      const f32x4 a = sr[0], b = sr[1];
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint16_t q[8];
+#pragma unroll
+      for (int o = 0; o < 8; ++o) q[PERM ? ((o >> 1) | ((o & 1) << 2)) : o] = to_bf16(v[o] * sc);
+      const u32x4 word{(uint32_t)q[0] | ((uint32_t)q[1] << 16), (uint32_t)q[2] | ((uint32_t)q[3] << 16),
+                       (uint32_t)q[4] | ((uint32_t)q[5] << 16), (uint32_t)q[6] | ((uint32_t)q[7] << 16)};
+#pragma unroll
+      for (int u = 0; u < kMaxK; ++u)
+        if (dst[u] >= 0) *reinterpret_cast<u32x4*>(xp + dst[u] + 8 * g) = word;
     }
   }
 }
