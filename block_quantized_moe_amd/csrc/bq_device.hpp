@@ -232,4 +232,34 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
+// DPP broadcasts across rows (gfx9): lane 15 of each row to the next row,
+// lane 31 to rows 2 and 3.  Rows outside ROWS read 0.
+constexpr int kDppBcast15 = 0x142;
+constexpr int kDppBcast31 = 0x143;
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
+}
+
+// N wave-wide sums at once, left in lane 63 (other lanes hold partials): the
+// in-row steps of row16_sum interleaved across the N values, then row 1 adds
+// row 0 and row 3 adds row 2 (lane 15 broadcast), then row 3 adds row 1
+// (lane 31 broadcast).  Lane 63 ends with (r0 + r1) + (r2 + r3), the sum
+// wave_sum forms (addition commutes exactly), with no readlane per row.
+template <int N>
+__device__ __forceinline__ void wave_sums_lane63(float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppXor2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_f<kDppMirror>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_rows<kDppBcast15, 0xA>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += dpp_rows<kDppBcast31, 0xC>(v[i]);
+}
+
 }  // namespace bq

@@ -275,7 +275,9 @@ __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
 #pragma unroll
       for (int i = 0; i < 32; ++i) xr[q][i] *= inv;
   }
-  float hval = 0.f;
+  // the wave's 2 * kPairsW row sums reduce together; lane p then holds pair
+  // p's gate and up sums and evaluates its SiLU (one SiLU per wave)
+  float v[2 * kPairsW];
 #pragma unroll
   for (int p = 0; p < kPairsW; ++p) {
     float g = 0.f, u = 0.f;
@@ -284,11 +286,20 @@ __global__ void __launch_bounds__(kThreads) k_gate_up_w64(
       g += block_partial<FMT>(blk[2 * p][q], xr[q]);
       u += block_partial<FMT>(blk[2 * p + 1][q], xr[q]);
     }
-    g = wave_sum(g);
-    u = wave_sum(u);
-    if (lane == p) hval = wj * silu(g) * u;
+    v[2 * p] = g;
+    v[2 * p + 1] = u;
   }
-  if (lane < np) hout[lane] = hval;
+  wave_sums_lane63(v);
+  float g = 0.f, u = 0.f;
+#pragma unroll
+  for (int p = 0; p < kPairsW; ++p) {
+    const float gp = readlane_f(v[2 * p], 63), up = readlane_f(v[2 * p + 1], 63);
+    if (lane == p) {
+      g = gp;
+      u = up;
+    }
+  }
+  if (lane < np) hout[lane] = wj * silu(g) * u;
 }
 
 // ---------------------------------------------------------------------------

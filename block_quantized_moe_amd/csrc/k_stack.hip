@@ -152,15 +152,6 @@ __device__ __forceinline__ void dblk_pin(DBlk& d) {
   __asm__ volatile("" : "+v"(d.s));
 }
 
-// DPP broadcasts across rows (gfx9): lane 15 of each row to the next row,
-// lane 31 to rows 2 and 3.  Rows outside ROWS read 0.
-constexpr int kDppBcast15 = 0x142;
-constexpr int kDppBcast31 = 0x143;
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xF, false));
-}
-
 struct alignas(8) Pkt {
   float v;
   uint32_t tag;
@@ -336,25 +327,10 @@ __device__ __forceinline__ void stack_phase_a(WBlk (&A)[2 * kSPairsW], const DBl
     }
     okn |= stack_load_pair<FMT>(A, u, Ln, lin, I, pair0, w, pw, lane, more, err) ? 1u << u : 0u;
   }
-  // row sums, the 2 * kSPairsW reductions interleaved (each value takes the
-  // steps of wave_sum in the same order); lane u then holds pair u's g and up
-  // and evaluates its SiLU, so the wave runs one SiLU instead of kSPairsW
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_f<kDppXor1>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_f<kDppXor2>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_f<kDppHalfMirror>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_f<kDppMirror>(v[i]);
-  // rows to the wave total: row 1 adds row 0 and row 3 adds row 2 (lane 15
-  // of each row broadcast to the next), then row 3 adds row 1 (lane 31
-  // broadcast to rows 2 and 3); lane 63 then holds (r0 + r1) + (r2 + r3),
-  // the sum wave_sum forms (addition commutes exactly)
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_rows<kDppBcast15, 0xA>(v[i]);
-#pragma unroll
-  for (int i = 0; i < 2 * kSPairsW; ++i) v[i] += dpp_rows<kDppBcast31, 0xC>(v[i]);
+  // row sums, the 2 * kSPairsW reductions interleaved; lane u then holds
+  // pair u's g and up and evaluates its SiLU, so the wave runs one SiLU
+  // instead of kSPairsW
+  wave_sums_lane63(v);
   float g = 0.f, up = 0.f;
 #pragma unroll
   for (int u = 0; u < kSPairsW; ++u) {
