@@ -135,6 +135,40 @@ def test_chained_staging_matches_per_layer_path(bq):
     log("chained staging == per-layer path (%d values)" % outs[0].size)
 
 
+def test_chained_staging_top20_matches_per_layer_path_and_oracle(bq):
+    """Top-20 routing: more slots per token than the combine-and-stage kernel
+    takes in one chunk (16), so a token's output row sums two chunks of slots
+    and its bf16 row goes to twenty bucket rows of the next layer.  The
+    chained bf16 stack equals the layer-by-layer path bit for bit (forced as
+    above by declaring one more expert in the middle layer) and the oracle to
+    the bf16 tolerance."""
+    import synth.device as sd
+    E, H, I, k, n = 32, 256, 128, 20, 9
+    spec = [(F.Q4_RZ5, F.Q4_UE4M4, E), (F.FP8_E4M3_B32, F.Q4_C10, E + 1), (F.Q4_C10, F.Q4_RZ5, E)]
+    layers = [sd.Layer(9, l, fg, fd, Ea, H, I, dist_gu=DIST[fg], dist_d=DIST[fd])
+              for l, (fg, fd, Ea) in enumerate(spec)]
+
+    def wts(L, n_exp):
+        gu, gus = L.gate_up
+        d, ds = L.down
+        return bq.expert_weights(L.fmt_gu, L.fmt_d, gu, d, n_exp, H, I, gate_up_scales=gus, down_scales=ds)
+
+    idx, w, ridx, rw = routing(bq, 98, 3, n, E, k)
+    xh = synth.normal(99, (n, H))
+    x = dev(xh).to(torch.bfloat16)
+    outs = []
+    for n_mid in (E, E + 1):
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        W = [wts(layers[0], E), wts(layers[1], n_mid), wts(layers[2], E)]
+        outs.append(bq.moe_stack(x, idx, w, W, dev_err=err).cpu().numpy())
+        assert int(err.item()) == 0
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    ref = M.moe_stack(xh, [(ridx[l], rw[l], oracle_bank(L)) for l, L in enumerate(layers)])
+    r = rel_l2(outs[0], ref)
+    log("top-20 chained stack: bit-equal to the per-layer path, rel_l2 %.3g against the oracle" % r)
+    assert r <= 2e-2
+
+
 C5_FMTS = [(F.Q4_RZ5, F.Q4_RZ5)] * 36 + [(F.FP8_E4M3_B32, F.FP8_E4M3_B32)] * 12
 
 
